@@ -1,0 +1,203 @@
+"""Seeded synthetic inputs for sink attention.
+
+This module only draws and packs inputs: lengths, page permutations, bf16 Q/K/V bit
+patterns and fp32 sink vectors. It contains none of the attention arithmetic, so both
+the CPU oracle and the GPU path can consume the same inputs without sharing any of
+the method's code.
+
+Shapes and distributions follow the workloads of the source pages: GPT-OSS-style GQA
+decode and prefill ("GPT-OSS on Day 0", section "Attention sinks"), the ragged
+embedding batches of "Fast Embeddings on GPUs" (section on ragged attention), and
+multi-token verification of "Accelerating Sonar through speculation" (MTP section).
+
+Recipe (fixed, documented in the design notes):
+  * ``numpy.random.default_rng(seed)``; draw order: lengths -> page permutation ->
+    Q -> K -> V -> sinks.
+  * Q/K/V are fp32 N(0, 1) rounded to bf16 with round-to-nearest-even.
+  * Sinks are fp32 ``sink_std * N(0, 1)``; ``sink_std=None`` means the sink is
+    disabled (-inf for every head).
+  * Uniform integer lengths are inclusive: ``rng.integers(lo, hi + 1)``.
+  * The paged KV pool holds exactly the pages the batch needs, in a seeded random
+    physical order; page-table entries past a sequence's last page are 0 and are
+    never dereferenced.
+  * KV cache layout is [num_pages, num_kv_heads, page_size, head_dim] ("HND").
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+
+__all__ = [
+    "VarlenSpec", "PagedSpec", "CONFIGS", "bf16_round_bits", "bf16_bits_to_f32",
+    "make_varlen", "make_paged", "scaled",
+]
+
+
+# ---------------------------------------------------------------------------------
+# bf16 bit handling (representation only)
+# ---------------------------------------------------------------------------------
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 with round-to-nearest-even; return uint16 bit patterns.
+
+    Inputs here are finite normals, so NaN handling is not needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return bf16_round_bits(x)
+
+
+def _sinks(rng: np.random.Generator, hq: int, std: Optional[float]) -> np.ndarray:
+    if std is None:
+        return np.full(hq, -np.inf, dtype=np.float32)
+    return (np.float32(std) * rng.standard_normal(size=hq, dtype=np.float32)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------------
+# Workload descriptions
+# ---------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class VarlenSpec:
+    """Packed variable-length self-attention (prefill / embedding), no KV cache."""
+    name: str
+    batch: int
+    seqlen: Tuple[int, int]          # inclusive uniform range; (n, n) for fixed length
+    hq: int
+    hkv: int
+    head_dim: int = 64
+    causal: bool = True
+    window: int = 0                  # <= 0: no window; else W keys including self
+    sink_std: Optional[float] = 1.0  # None: sinks disabled (-inf)
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+
+@dataclass(frozen=True)
+class PagedSpec:
+    """Decode / verify against a paged KV cache (q_len new tokens per sequence)."""
+    name: str
+    batch: int
+    q_len: int
+    kv_len: Tuple[int, int]          # inclusive uniform range; includes the q_len new tokens
+    hq: int
+    hkv: int
+    head_dim: int = 64
+    page_size: int = 16
+    kv_chunk: int = 512
+    causal: bool = True
+    window: int = 0
+    sink_std: Optional[float] = 2.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+
+CONFIGS = {
+    # Tiny causal GQA 4:1, single sequence of 16 tokens, single KV chunk.
+    "tiny_causal": VarlenSpec("tiny_causal", batch=1, seqlen=(16, 16), hq=4, hkv=1,
+                              causal=True, sink_std=1.0, seed=0),
+    # Paged single-token decode, 64 sequences, KV 1024..8192, 64/8 heads, 512-token chunks.
+    "paged_decode": PagedSpec("paged_decode", batch=64, q_len=1, kv_len=(1024, 8192), hq=64, hkv=8,
+                              page_size=16, kv_chunk=512, sink_std=2.0, seed=1),
+    # Causal prefill 8 x 4096 packed; the same inputs also run with a 128-key window.
+    "causal_prefill": VarlenSpec("causal_prefill", batch=8, seqlen=(4096, 4096), hq=64, hkv=8,
+                                 causal=True, window=0, sink_std=2.0, seed=2),
+    "window_prefill": VarlenSpec("window_prefill", batch=8, seqlen=(4096, 4096), hq=64, hkv=8,
+                                 causal=True, window=128, sink_std=2.0, seed=2),
+    # Speculative verify: 5 query tokens per sequence, causal inside the block.
+    "verify": PagedSpec("verify", batch=32, q_len=5, kv_len=(2048, 16384), hq=64, hkv=8,
+                        page_size=16, kv_chunk=512, sink_std=2.0, seed=3),
+    # Bidirectional MHA embedding batch; pass A with sinks disabled, pass B with N(0,1) sinks.
+    "embed_nosink": VarlenSpec("embed_nosink", batch=512, seqlen=(16, 512), hq=16, hkv=16,
+                               causal=False, sink_std=None, seed=4),
+    "embed_sink": VarlenSpec("embed_sink", batch=512, seqlen=(16, 512), hq=16, hkv=16,
+                             causal=False, sink_std=1.0, seed=4),
+}
+
+
+def scaled(spec, **changes):
+    """A copy of ``spec`` with some fields replaced (smaller parity-test variants)."""
+    return dataclasses.replace(spec, **changes)
+
+
+# ---------------------------------------------------------------------------------
+# Generators
+# ---------------------------------------------------------------------------------
+def _draw_lengths(rng: np.random.Generator, batch: int, lo_hi: Tuple[int, int]) -> np.ndarray:
+    lo, hi = lo_hi
+    if lo == hi:
+        return np.full(batch, lo, dtype=np.int32)
+    return rng.integers(lo, hi + 1, size=batch).astype(np.int32)
+
+
+def make_varlen(spec: VarlenSpec, seqlens: Optional[np.ndarray] = None) -> dict:
+    """Inputs for packed varlen attention.
+
+    Returns q [T, hq, d], k/v [T, hkv, d] as uint16 bf16 bits, sinks fp32 [hq],
+    cu_seqlens int32 [batch + 1] (the same array serves Q and KV) and max_seqlen.
+    ``seqlens`` overrides the drawn lengths (edge-case tests); the draw order of the
+    remaining tensors is unchanged.
+    """
+    rng = np.random.default_rng(spec.seed)
+    lens = _draw_lengths(rng, spec.batch, spec.seqlen)
+    if seqlens is not None:
+        lens = np.asarray(seqlens, dtype=np.int32)
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens, dtype=np.int64).astype(np.int32)
+    total = int(cu[-1])
+    q = _normal_bf16(rng, (total, spec.hq, spec.head_dim))
+    k = _normal_bf16(rng, (total, spec.hkv, spec.head_dim))
+    v = _normal_bf16(rng, (total, spec.hkv, spec.head_dim))
+    sinks = _sinks(rng, spec.hq, spec.sink_std)
+    return dict(q=q, k=k, v=v, sinks=sinks, cu_seqlens=cu, seqlens=lens,
+                max_seqlen=int(lens.max()) if len(lens) else 0)
+
+
+def make_paged(spec: PagedSpec, kv_lens: Optional[np.ndarray] = None,
+               max_pages_per_seq: Optional[int] = None) -> dict:
+    """Inputs for paged decode / verify.
+
+    Returns q [batch * q_len, hq, d] bits, k_cache / v_cache [num_pages, hkv, page, d]
+    bits, page_table int32 [batch, max_pages_per_seq], kv_lens int32 [batch] and sinks
+    fp32 [hq]. Row ``b * q_len + t`` of q is query token t of sequence b; its absolute
+    position is ``kv_lens[b] - q_len + t``.
+    """
+    rng = np.random.default_rng(spec.seed)
+    lens = _draw_lengths(rng, spec.batch, spec.kv_len)
+    if kv_lens is not None:
+        lens = np.asarray(kv_lens, dtype=np.int32)
+    P = spec.page_size
+    npages_b = (lens.astype(np.int64) + P - 1) // P
+    num_pages = int(npages_b.sum())
+    perm = rng.permutation(num_pages).astype(np.int32)
+    if max_pages_per_seq is None:
+        max_pages_per_seq = max(1, -(-max(spec.kv_len[1], int(lens.max()) if len(lens) else 0) // P))
+    table = np.zeros((len(lens), max_pages_per_seq), dtype=np.int32)
+    off = 0
+    for b, n in enumerate(npages_b):
+        table[b, :n] = perm[off:off + n]
+        off += int(n)
+    q = _normal_bf16(rng, (len(lens) * spec.q_len, spec.hq, spec.head_dim))
+    pool = max(num_pages, 1)
+    k_cache = _normal_bf16(rng, (pool, spec.hkv, P, spec.head_dim))
+    v_cache = _normal_bf16(rng, (pool, spec.hkv, P, spec.head_dim))
+    sinks = _sinks(rng, spec.hq, spec.sink_std)
+    return dict(q=q, k_cache=k_cache, v_cache=v_cache, page_table=table, kv_lens=lens.astype(np.int32),
+                sinks=sinks, num_pages=pool, max_kv_len=int(lens.max()) if len(lens) else 0)
