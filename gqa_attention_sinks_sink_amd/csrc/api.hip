@@ -1,0 +1,226 @@
+// C ABI of libattnsink.so: argument validation, workspace layout and kernel launches.
+// Every check runs on the host before anything is enqueued; nothing here allocates,
+// frees or synchronises.
+#include <climits>
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/attn_sink.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace attn_sink;
+
+namespace {
+
+constexpr int32_t kSupportedHeadDim = 64;
+constexpr int32_t kMaxQLen = 8;
+constexpr int32_t kMaxColumns = 64;   // q_len * (num_q_heads / num_kv_heads) per decode workgroup
+constexpr int64_t kMaxGridY = 65535;
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+inline int32_t ilog2(int32_t x) {
+  int32_t s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+// Effective chunk length: kv_chunk if positive, else one chunk covering max_kv_len (rounded
+// up to the kernel's 64-key granularity and to whole pages).
+inline int64_t effective_chunk(int32_t kv_chunk, int32_t max_kv_len, int32_t page_size) {
+  if (kv_chunk > 0) return kv_chunk;
+  int64_t g = page_size > 64 ? page_size : 64;
+  int64_t L = max_kv_len > 0 ? max_kv_len : 1;
+  return ((L + g - 1) / g) * g;
+}
+
+struct DecodeLayout {
+  int64_t rows, chunks, partials;
+  size_t off_indptr, off_counts, off_o, off_lse, total;
+};
+
+inline bool decode_layout(int32_t batch, int32_t q_len, int32_t max_kv_len, int32_t num_q_heads,
+                          int64_t chunk, DecodeLayout* out) {
+  if (batch < 0 || q_len < 1 || max_kv_len < 0 || num_q_heads <= 0 || chunk <= 0) return false;
+  DecodeLayout l;
+  l.rows = (int64_t)batch * q_len;
+  l.chunks = (max_kv_len + chunk - 1) / chunk;
+  if (l.chunks < 1) l.chunks = 1;
+  l.partials = l.rows * l.chunks;
+  if (l.partials > INT32_MAX / 2) return false;
+  l.off_indptr = 0;
+  l.off_counts = align256(sizeof(int32_t) * (size_t)(l.rows + 1));
+  l.off_o = l.off_counts + align256(sizeof(int32_t) * (size_t)l.rows);
+  l.off_lse = l.off_o + align256(sizeof(float) * (size_t)l.partials * num_q_heads * kSupportedHeadDim);
+  l.total = l.off_lse + align256(sizeof(float) * (size_t)l.partials * num_q_heads);
+  *out = l;
+  return true;
+}
+
+inline attn_sink_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_sink_status_string(attn_sink_status status) {
+  switch (status) {
+    case ATTN_SINK_OK: return "ok";
+    case ATTN_SINK_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_SINK_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_SINK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case ATTN_SINK_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_sink_version(void) { return "attn_sink 0.1.0 gfx950"; }
+
+attn_sink_status attn_sink_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t batch,
+                                   int32_t total_q, int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                                   int32_t causal, int32_t window, void* out, float* lse, void* stream) {
+  if (batch < 0 || total_q < 0 || total_kv < 0 || max_seqlen_q < 0 || max_seqlen_kv < 0) return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kSupportedHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr) return ATTN_SINK_ERR_INVALID_ARG;
+  if (total_kv > 0 && (k == nullptr || v == nullptr)) return ATTN_SINK_ERR_INVALID_ARG;
+  const int32_t group = num_q_heads / num_kv_heads;
+  int32_t gp = 1;
+  while (gp < 16 && group % (gp * 2) == 0) gp *= 2;
+  const int64_t tiles = ((int64_t)max_seqlen_q + (128 / gp) - 1) / (128 / gp);
+  if (tiles * batch > INT32_MAX || (int64_t)num_kv_heads * (group / gp) > kMaxGridY) return ATTN_SINK_ERR_UNSUPPORTED;
+
+  PrefillParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.sinks = sinks;
+  p.cu_q = cu_seqlens_q;
+  p.cu_kv = cu_seqlens_kv;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.batch = batch;
+  p.total_q = total_q;
+  p.total_kv = total_kv;
+  p.max_q = max_seqlen_q;
+  p.max_kv = max_seqlen_kv;
+  p.hq = num_q_heads;
+  p.hkv = num_kv_heads;
+  p.group = group;
+  p.causal = causal != 0;
+  p.window = window > 0 ? window : 0;
+  p.scale_log2 = softmax_scale * kLog2e;
+  return hip_status(launch_prefill(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t attn_sink_decode_workspace_size(int32_t batch, int32_t q_len, int32_t max_kv_len, int32_t num_q_heads,
+                                       int32_t head_dim, int32_t kv_chunk) {
+  if (head_dim != kSupportedHeadDim) return 0;
+  DecodeLayout l;
+  // The page size only rounds the single-chunk length up; it never changes the chunk count.
+  if (!decode_layout(batch, q_len, max_kv_len, num_q_heads, effective_chunk(kv_chunk, max_kv_len, 16), &l)) return 0;
+  return l.total;
+}
+
+attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+                                        const int32_t* kv_lens, const float* sinks, int32_t batch, int32_t q_len,
+                                        int32_t max_kv_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t page_size, float softmax_scale, int32_t causal,
+                                        int32_t window, int32_t kv_chunk, void* workspace, size_t workspace_bytes,
+                                        void* out, float* lse, void* stream) {
+  if (batch < 0 || max_kv_len < 0 || max_pages_per_seq < 1 || num_pages < 1 || q_len < 1) return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kSupportedHeadDim || q_len > kMaxQLen) return ATTN_SINK_ERR_UNSUPPORTED;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if ((int64_t)q_len * group > kMaxColumns) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size < 16 || page_size > 256) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (kv_chunk > 0 && (kv_chunk % 64 != 0 || kv_chunk % page_size != 0)) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (num_kv_heads > kMaxGridY) return ATTN_SINK_ERR_UNSUPPORTED;
+  const int64_t chunk = effective_chunk(kv_chunk, max_kv_len, page_size);
+  if (chunk > INT32_MAX / 2) return ATTN_SINK_ERR_UNSUPPORTED;
+  DecodeLayout lay;
+  if (!decode_layout(batch, q_len, max_kv_len, num_q_heads, chunk, &lay)) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (lay.chunks * batch > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch == 0) return ATTN_SINK_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || page_table == nullptr || kv_lens == nullptr ||
+      out == nullptr || workspace == nullptr)
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_SINK_ERR_INVALID_ARG;
+  if (workspace_bytes < attn_sink_decode_workspace_size(batch, q_len, max_kv_len, num_q_heads, head_dim, kv_chunk) ||
+      workspace_bytes < lay.total)
+    return ATTN_SINK_ERR_WORKSPACE_TOO_SMALL;
+
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const uint16_t*>(k_cache);
+  p.v_cache = static_cast<const uint16_t*>(v_cache);
+  p.page_table = page_table;
+  p.kv_lens = kv_lens;
+  p.sinks = sinks;
+  p.indptr = reinterpret_cast<int32_t*>(ws + lay.off_indptr);
+  p.counts = reinterpret_cast<int32_t*>(ws + lay.off_counts);
+  p.o_part = reinterpret_cast<float*>(ws + lay.off_o);
+  p.lse_part = reinterpret_cast<float*>(ws + lay.off_lse);
+  p.batch = batch;
+  p.q_len = q_len;
+  p.max_kv_len = max_kv_len;
+  p.hq = num_q_heads;
+  p.hkv = num_kv_heads;
+  p.group = group;
+  p.page_size = page_size;
+  p.page_shift = ilog2(page_size);
+  p.max_pages = max_pages_per_seq;
+  p.num_pages = num_pages;
+  p.kv_chunk = (int)chunk;
+  p.causal = causal != 0;
+  p.window = window > 0 ? window : 0;
+  p.scale_log2 = softmax_scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_decode_split(p, (int)lay.chunks, s);
+  if (e != hipSuccess) return ATTN_SINK_ERR_HIP;
+
+  MergeParams mp;
+  mp.o_part = p.o_part;
+  mp.lse_part = p.lse_part;
+  mp.indptr = p.indptr;
+  mp.out = static_cast<uint16_t*>(out);
+  mp.lse = lse;
+  mp.num_partials = (int)lay.partials;
+  mp.rows = (int)lay.rows;
+  mp.hq = num_q_heads;
+  return hip_status(launch_merge(mp, s));
+}
+
+attn_sink_status attn_sink_merge_partials(const float* o_partial, const float* lse_partial, int32_t num_partials,
+                                          const int32_t* partial_indptr, int32_t num_rows, int32_t num_q_heads,
+                                          int32_t head_dim, void* out, float* lse, void* stream) {
+  if (num_partials < 0 || num_rows < 0 || num_q_heads <= 0) return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kSupportedHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
+  if ((num_q_heads + 3) / 4 > kMaxGridY) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (num_rows == 0) return ATTN_SINK_OK;
+  if (partial_indptr == nullptr || out == nullptr) return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_partials > 0 && (o_partial == nullptr || lse_partial == nullptr)) return ATTN_SINK_ERR_INVALID_ARG;
+  MergeParams mp;
+  mp.o_part = o_partial;
+  mp.lse_part = lse_partial;
+  mp.indptr = partial_indptr;
+  mp.out = static_cast<uint16_t*>(out);
+  mp.lse = lse;
+  mp.num_partials = num_partials;
+  mp.rows = num_rows;
+  mp.hq = num_q_heads;
+  return hip_status(launch_merge(mp, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

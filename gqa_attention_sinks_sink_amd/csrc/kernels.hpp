@@ -1,0 +1,53 @@
+// Kernel parameter blocks and launchers (internal to libattnsink.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn_sink {
+
+struct DecodeParams {
+  const uint16_t* q;        // bf16 [batch*q_len, hq, 64]
+  const uint16_t* k_cache;  // bf16 [num_pages, hkv, page_size, 64]
+  const uint16_t* v_cache;
+  const int32_t* page_table;  // [batch, max_pages]
+  const int32_t* kv_lens;     // [batch]
+  const float* sinks;         // [hq] or nullptr
+  int32_t* indptr;            // workspace: [batch*q_len + 1]
+  int32_t* counts;            // workspace: [batch*q_len]
+  float* o_part;              // workspace: [n_partials, hq, 64]
+  float* lse_part;            // workspace: [n_partials, hq]
+  int batch, q_len, max_kv_len, hq, hkv, group;
+  int page_size, page_shift, max_pages, num_pages;
+  int kv_chunk, causal, window;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+struct MergeParams {
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* indptr;
+  uint16_t* out;  // bf16 [rows, hq, 64]
+  float* lse;     // [rows, hq] or nullptr
+  int num_partials, rows, hq;
+};
+
+struct PrefillParams {
+  const uint16_t* q;  // bf16 [total_q, hq, 64]
+  const uint16_t* k;  // bf16 [total_kv, hkv, 64]
+  const uint16_t* v;
+  const float* sinks;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  uint16_t* out;  // bf16 [total_q, hq, 64]
+  float* lse;     // [total_q, hq] or nullptr
+  int batch, total_q, total_kv, max_q, max_kv;
+  int hq, hkv, group, causal, window;
+  float scale_log2;
+};
+
+hipError_t launch_decode_split(const DecodeParams& p, int max_chunks, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+}  // namespace attn_sink

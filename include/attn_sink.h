@@ -1,0 +1,186 @@
+/*
+ * attn_sink.h -- C ABI of libattnsink.so: grouped-query attention whose softmax
+ * includes a learned per-head sink logit, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (source: "GPT-OSS on Day 0", section "Attention sinks"): every query
+ * head h carries a sink logit sink[h] that joins the softmax over the scaled Q.K
+ * scores of its row and has no value vector. For a query row with visible keys J:
+ *     M   = max(max_{j in J} s_j, sink[h]),          s_j = softmax_scale * q . k_j
+ *     D   = sum_{j in J} exp(s_j - M) + exp(sink[h] - M)
+ *     out = sum_{j in J} exp(s_j - M) v_j / D        (bf16)
+ *     lse = M + ln D                                  (fp32, natural log, sink included)
+ * The kernels compute this with an online (streaming) softmax whose running maximum
+ * is seeded with the head's sink in the first KV chunk only; when the KV range is
+ * split, chunk partials are combined by a log-sum-exp merge (same section: heads and
+ * the KV length are processed in parallel).
+ *
+ * Conventions shared by every entry point
+ *   - Element types: Q, K, V and `out` are bf16 (passed as void*); sinks, lse and all
+ *     partials are fp32; indices and lengths are int32.
+ *   - All tensor pointers are DEVICE pointers on the current HIP device; the caller owns
+ *     every buffer (workspace included). The library never allocates, frees or
+ *     synchronises; all work is enqueued on `stream` (a hipStream_t; NULL = default
+ *     stream). Launch shapes depend only on host scalars, so calls may be captured
+ *     into a HIP graph.
+ *   - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   - Masks are computed from indices (no mask tensor). With Lq query tokens and Lk keys
+ *     in a sequence, query token t sits at absolute position p = Lk - Lq + t (new tokens
+ *     are the last ones). causal != 0: key j visible iff j <= p. window > 0: key j also
+ *     needs p - j < window (window keys including the query's own position).
+ *   - `sinks` may be NULL: every head then behaves as sink = -inf (plain attention).
+ *     Individual entries may be -inf.
+ *   - A query row with no visible key returns out = 0 and lse = sink[h] (-inf when the
+ *     sink is disabled); no NaN is produced.
+ *   - head_dim must be 64.
+ *   - Errors: arguments are validated on the host before anything is enqueued; invalid
+ *     arguments return ATTN_SINK_ERR_INVALID_ARG and unsupported shapes
+ *     ATTN_SINK_ERR_UNSUPPORTED, with nothing launched. A failed launch returns
+ *     ATTN_SINK_ERR_HIP. Device-side faults surface at the caller's next
+ *     synchronisation. Nothing aborts the process.
+ *   - Memory safety against bad device metadata: sequence lengths, cu_seqlens offsets and
+ *     page ids read on the device are clamped into the ranges the host scalars declare,
+ *     so inconsistent metadata yields wrong numbers for the affected rows, never an
+ *     out-of-bounds access.
+ */
+#ifndef ATTN_SINK_H_
+#define ATTN_SINK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_SINK_OK = 0,
+  ATTN_SINK_ERR_INVALID_ARG = 1,
+  ATTN_SINK_ERR_UNSUPPORTED = 2,
+  ATTN_SINK_ERR_WORKSPACE_TOO_SMALL = 3,
+  ATTN_SINK_ERR_HIP = 4
+} attn_sink_status;
+
+/*
+ * Packed variable-length self-attention without a KV cache: causal prefill,
+ * sliding-window prefill and bidirectional (embedding) batches ("GPT-OSS on Day 0",
+ * section "Attention sinks": the same kernel family serves prefill; "Fast Embeddings on
+ * GPUs", ragged-attention section: embedding batches run ragged, without padding).
+ *
+ *   q            bf16 [total_q, num_q_heads, 64], contiguous.
+ *   k, v         bf16 [total_kv, num_kv_heads, 64], contiguous.
+ *   sinks        fp32 [num_q_heads] or NULL.
+ *   cu_seqlens_q, cu_seqlens_kv
+ *                int32 [batch + 1] on the device, non-decreasing, starting at 0:
+ *                sequence b owns Q rows [cu_q[b], cu_q[b+1]) and KV rows
+ *                [cu_kv[b], cu_kv[b+1]). The same pointer may be passed for both.
+ *   total_q, total_kv
+ *                rows in q and in k/v (bounds for the clamping of device offsets).
+ *   max_seqlen_q, max_seqlen_kv
+ *                host upper bounds of the per-sequence lengths (they size the launch
+ *                grid; longer sequences are truncated to them).
+ *   softmax_scale  multiplies q.k (e.g. 1/sqrt(64)); the sink is NOT scaled.
+ *   causal, window  see the conventions above (window <= 0: no window).
+ *   out          bf16 [total_q, num_q_heads, 64].
+ *   lse          fp32 [total_q, num_q_heads] or NULL.
+ * Constraints: batch >= 0, num_q_heads % num_kv_heads == 0, head_dim == 64,
+ * softmax_scale finite and > 0; q, k, v, out and the cu_seqlens pointers non-NULL when
+ * batch > 0 and total_q > 0.
+ */
+attn_sink_status attn_sink_prefill(
+    const void* q, const void* k, const void* v, const float* sinks,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t max_seqlen_q, int32_t max_seqlen_kv,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    float softmax_scale, int32_t causal, int32_t window,
+    void* out, float* lse, void* stream);
+
+/*
+ * Paged decode (q_len = 1) and multi-token verify decode (q_len 2..8, causal inside the
+ * block) against a paged KV cache, split along the KV length into kv_chunk-token
+ * chunks whose partials are merged by log-sum-exp ("GPT-OSS on Day 0", section
+ * "Attention sinks": split across blocks along the sequence, sink only in the first
+ * chunk; "Fast Embeddings on GPUs": paged decode; "Accelerating Sonar through
+ * speculation": verification of several draft tokens per sequence).
+ *
+ *   q            bf16 [batch * q_len, num_q_heads, 64]; row b*q_len + t is query token t
+ *                of sequence b, at absolute position kv_lens[b] - q_len + t.
+ *   k_cache, v_cache
+ *                bf16 [num_pages, num_kv_heads, page_size, 64] ("HND": one page of one KV
+ *                head is a contiguous page_size x 64 block). Token j of sequence b is in
+ *                physical page page_table[b * max_pages_per_seq + j / page_size], slot
+ *                j % page_size.
+ *   page_table   int32 [batch, max_pages_per_seq] on the device.
+ *   kv_lens      int32 [batch] on the device; KV length of each sequence INCLUDING its
+ *                q_len new tokens (already appended). Clamped to
+ *                [0, min(max_kv_len, max_pages_per_seq * page_size)].
+ *   sinks        fp32 [num_q_heads] or NULL.
+ *   max_kv_len   host upper bound of kv_lens (sizes the grid and the workspace).
+ *   kv_chunk     tokens per split-KV chunk: a positive multiple of 64 that is also a
+ *                multiple of page_size; <= 0 means one chunk spanning max_kv_len.
+ *   workspace    caller-owned device buffer of at least
+ *                attn_sink_decode_workspace_size(...) bytes, 256-byte aligned. Layout, with
+ *                R = batch * q_len rows, C = chunks per row bound = max(1, ceil(max_kv_len /
+ *                kv_chunk)), NP = R * C, each region starting at a 256-byte boundary:
+ *                  int32 partial_indptr[R + 1]   (plan: row r owns partials
+ *                                                 [indptr[r], indptr[r+1]); exclusive scan)
+ *                  int32 chunk_counts[R]          (plan: n_r = max(1, ceil(L_b / kv_chunk)))
+ *                  fp32  o_partial[NP][num_q_heads][64]  (chunk outputs, each normalised)
+ *                  fp32  lse_partial[NP][num_q_heads]    (chunk log-sum-exp, natural log)
+ *                Partial indptr[r] + c holds chunk c of row r; chunk 0 carries the sink.
+ *                The plan and the partials are valid after the call completes.
+ *   out, lse     bf16 [batch * q_len, num_q_heads, 64]; fp32 [batch * q_len, num_q_heads]
+ *                or NULL.
+ * Constraints: 1 <= q_len <= 8, q_len * (num_q_heads / num_kv_heads) <= 64,
+ * page_size a power of two in [16, 256] and at most kv_chunk, head_dim == 64,
+ * num_pages >= 1, max_pages_per_seq >= 1. Enqueues two kernels (split-KV chunks, then
+ * the merge).
+ */
+attn_sink_status attn_sink_decode_paged(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    const int32_t* kv_lens, const float* sinks,
+    int32_t batch, int32_t q_len, int32_t max_kv_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    float softmax_scale, int32_t causal, int32_t window, int32_t kv_chunk,
+    void* workspace, size_t workspace_bytes,
+    void* out, float* lse, void* stream);
+
+/*
+ * Bytes of workspace attn_sink_decode_paged needs for these host scalars (0 if they are
+ * invalid). Monotone non-decreasing in batch, q_len, max_kv_len and num_q_heads.
+ */
+size_t attn_sink_decode_workspace_size(int32_t batch, int32_t q_len, int32_t max_kv_len,
+                                       int32_t num_q_heads, int32_t head_dim, int32_t kv_chunk);
+
+/*
+ * Log-sum-exp merge of split-KV partials ("GPT-OSS on Day 0", section "Attention
+ * sinks": attention split into several blocks along the sequence). For row r and head h,
+ * over partials p in [partial_indptr[r], partial_indptr[r+1]):
+ *     LSE = ln sum_p exp(lse_partial[p][h]),  out = sum_p exp(lse_partial[p][h] - LSE) o_partial[p][h]
+ * Partials with lse = -inf carry weight 0; a row whose partials are all -inf (or that has
+ * none) returns out = 0, lse = -inf.
+ *
+ *   o_partial    fp32 [num_partials, num_q_heads, 64]; each partial already normalised.
+ *   lse_partial  fp32 [num_partials, num_q_heads], natural log.
+ *   partial_indptr  int32 [num_rows + 1] on the device, non-decreasing; entries are
+ *                clamped to [0, num_partials].
+ *   out, lse     bf16 [num_rows, num_q_heads, 64]; fp32 [num_rows, num_q_heads] or NULL.
+ */
+attn_sink_status attn_sink_merge_partials(
+    const float* o_partial, const float* lse_partial, int32_t num_partials,
+    const int32_t* partial_indptr, int32_t num_rows,
+    int32_t num_q_heads, int32_t head_dim,
+    void* out, float* lse, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* attn_sink_status_string(attn_sink_status status);
+
+/* Library version string, e.g. "attn_sink 0.1.0 gfx950". */
+const char* attn_sink_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SINK_H_ */

@@ -1,0 +1,154 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status codes before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_sink.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = 0, 1, 2, 3, 4
+FAKE = 0x100000  # a non-NULL, 256-aligned address; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def amd():
+    from gqa_attention_sinks_sink_amd.build import LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import gqa_attention_sinks_sink_amd as amd
+    return amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_sink_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("attn_sink_prefill", "attn_sink_decode_paged", "attn_sink_merge_partials",
+              "attn_sink_decode_workspace_size", "attn_sink_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(amd):
+    for name in declared_functions():
+        assert hasattr(amd.lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", amd.lib._name], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(\S+)", nm))
+    assert set(declared_functions()) <= exported
+    assert set(amd.EXPORTED_SYMBOLS) == set(declared_functions())
+
+
+def test_status_strings_and_version(amd):
+    assert amd.attn_sink_status_string(0) == "ok"
+    assert "workspace" in amd.attn_sink_status_string(3)
+    assert amd.attn_sink_status_string(99) == "unknown status"
+    assert "gfx950" in amd.attn_sink_version()
+
+
+def test_workspace_size_layout_and_monotone(amd):
+    ws = amd.attn_sink_decode_workspace_size
+    assert ws(64, 1, 8192, 64, 64, 512) == amd.decode_workspace_layout(64, 1, 8192, 64, 512)["total"]
+    assert ws(32, 5, 16384, 64, 64, 512) == amd.decode_workspace_layout(32, 5, 16384, 64, 512)["total"]
+    assert ws(4, 1, 100, 8, 64, 0) == amd.decode_workspace_layout(4, 1, 100, 8, 0)["total"]
+    assert ws(4, 1, 100, 8, 128, 512) == 0          # unsupported head_dim
+    assert ws(-1, 1, 100, 8, 64, 512) == 0
+    prev = 0
+    for L in (0, 1, 511, 512, 513, 4096, 9000):
+        cur = ws(8, 2, L, 16, 64, 512)
+        assert cur >= prev and cur % 256 == 0
+        prev = cur
+    assert ws(9, 2, 9000, 16, 64, 512) >= ws(8, 2, 9000, 16, 64, 512)
+    assert ws(8, 3, 9000, 16, 64, 512) >= ws(8, 2, 9000, 16, 64, 512)
+    assert ws(8, 2, 9000, 32, 64, 512) >= ws(8, 2, 9000, 16, 64, 512)
+
+
+def _prefill(amd, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=None, cu_q=FAKE, cu_kv=FAKE, batch=1, total_q=16, total_kv=16,
+             max_q=16, max_kv=16, hq=4, hkv=1, d=64, scale=0.125, causal=1, window=0, out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return amd.lib.attn_sink_prefill(a["q"], a["k"], a["v"], a["sinks"], a["cu_q"], a["cu_kv"], a["batch"],
+                                     a["total_q"], a["total_kv"], a["max_q"], a["max_kv"], a["hq"], a["hkv"], a["d"],
+                                     a["scale"], a["causal"], a["window"], a["out"], a["lse"], a["stream"])
+
+
+def test_prefill_argument_errors(amd):
+    assert _prefill(amd, d=128) == UNSUPPORTED
+    assert _prefill(amd, hq=6, hkv=4) == INVALID
+    assert _prefill(amd, hkv=0) == INVALID
+    assert _prefill(amd, scale=0.0) == INVALID
+    assert _prefill(amd, scale=float("nan")) == INVALID
+    assert _prefill(amd, scale=float("inf")) == INVALID
+    assert _prefill(amd, batch=-1) == INVALID
+    assert _prefill(amd, total_q=-5) == INVALID
+    assert _prefill(amd, q=None) == INVALID
+    assert _prefill(amd, out=None) == INVALID
+    assert _prefill(amd, cu_q=None) == INVALID
+    assert _prefill(amd, k=None) == INVALID
+    # nothing to do: accepted without launching anything
+    assert _prefill(amd, batch=0, q=None, out=None) == OK
+    assert _prefill(amd, total_q=0, q=None, out=None) == OK
+
+
+def _decode(amd, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, max_pages=512, num_pages=100, kv_lens=FAKE, sinks=None, batch=4,
+             q_len=1, max_kv=8192, hq=64, hkv=8, d=64, page=16, scale=0.125, causal=1, window=0, chunk=512,
+             ws=FAKE, ws_bytes=1 << 40, out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return amd.lib.attn_sink_decode_paged(a["q"], a["k"], a["v"], a["table"], a["max_pages"], a["num_pages"],
+                                          a["kv_lens"], a["sinks"], a["batch"], a["q_len"], a["max_kv"], a["hq"],
+                                          a["hkv"], a["d"], a["page"], a["scale"], a["causal"], a["window"],
+                                          a["chunk"], a["ws"], a["ws_bytes"], a["out"], a["lse"], a["stream"])
+
+
+def test_decode_argument_errors(amd):
+    assert _decode(amd, d=128) == UNSUPPORTED
+    assert _decode(amd, q_len=9) == UNSUPPORTED
+    assert _decode(amd, q_len=0) == INVALID
+    assert _decode(amd, hq=128, hkv=1) == UNSUPPORTED      # 128 columns per KV head
+    assert _decode(amd, q_len=8, hq=72, hkv=8) == UNSUPPORTED   # 8 x 9 = 72 columns
+    assert _decode(amd, page=24) == UNSUPPORTED
+    assert _decode(amd, page=8) == UNSUPPORTED
+    assert _decode(amd, page=512) == UNSUPPORTED
+    assert _decode(amd, chunk=100) == UNSUPPORTED
+    assert _decode(amd, chunk=64, page=128) == UNSUPPORTED
+    assert _decode(amd, hq=60, hkv=8) == INVALID
+    assert _decode(amd, scale=-1.0) == INVALID
+    assert _decode(amd, num_pages=0) == INVALID
+    assert _decode(amd, max_pages=0) == INVALID
+    assert _decode(amd, max_kv=-1) == INVALID
+    assert _decode(amd, q=None) == INVALID
+    assert _decode(amd, table=None) == INVALID
+    assert _decode(amd, ws=None) == INVALID
+    assert _decode(amd, ws=FAKE + 16) == INVALID             # workspace must be 256-byte aligned
+    need = amd.attn_sink_decode_workspace_size(4, 1, 8192, 64, 64, 512)
+    assert _decode(amd, ws_bytes=need - 1) == WS_SMALL
+    assert _decode(amd, ws_bytes=0) == WS_SMALL
+    assert _decode(amd, batch=0, q=None, ws=None) == OK
+
+
+def test_merge_argument_errors(amd):
+    f = amd.lib.attn_sink_merge_partials
+    assert f(FAKE, FAKE, 10, FAKE, 4, 8, 128, FAKE, None, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, -1, FAKE, 4, 8, 64, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 10, FAKE, -4, 8, 64, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 10, FAKE, 4, 0, 64, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 10, None, 4, 8, 64, FAKE, None, None) == INVALID
+    assert f(None, FAKE, 10, FAKE, 4, 8, 64, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 10, FAKE, 4, 8, 64, None, None, None) == INVALID
+    assert f(None, None, 0, None, 0, 8, 64, None, None, None) == OK
+
+
+def test_binding_refuses_cpu_tensors(amd):
+    import torch
+    q = torch.zeros(16, 4, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 16], dtype=torch.int32)
+    with pytest.raises((TypeError, ValueError, RuntimeError)):
+        amd.attn_sink_prefill(q.float(), q, q, None, cu, cu, 16, 16)

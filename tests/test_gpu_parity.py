@@ -1,0 +1,332 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle on the same
+seeded inputs.
+
+Bar (fixed for this method): bf16 outputs within |err| <= 1e-2 + 1e-2*|ref|, LSE within
+1e-3 absolute, integer plan outputs bit-exact, page-pool permutation bit-identical.
+Small cases run the whole oracle; full-size workloads are checked on sampled rows.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_varlen, scaled  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL, LSE_TOL = 1e-2, 1e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def amd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_attention_sinks_sink_amd as amd
+    return amd
+
+
+DEV = "cuda:0"
+
+
+def tbits(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def f64(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def out_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def assert_close(out, lse, ro, rl, what):
+    sel = ~np.isnan(rl)
+    o = out[sel]
+    r = ro[sel]
+    excess = np.abs(o - r) - (ATOL + RTOL * np.abs(r))
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    assert excess.max() <= 0, f"{what}: out max excess {excess.max():.3e} (max err {np.abs(o - r).max():.3e})"
+    if lse is not None:
+        l, rr = lse[sel], rl[sel]
+        inf = np.isinf(rr)
+        assert np.array_equal(np.isinf(l), inf) and np.array_equal(l[inf], rr[inf]), f"{what}: lse inf pattern"
+        if (~inf).any():
+            err = np.abs(l[~inf] - rr[~inf]).max()
+            assert err <= LSE_TOL, f"{what}: lse max err {err:.3e}"
+
+
+# -------------------------------------------------------------------------------------------
+# prefill / embedding
+# -------------------------------------------------------------------------------------------
+def run_prefill(amd, inp, spec, sinks=True, cu_kv=None, k=None, v=None, max_kv=None):
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(DEV)
+    cukv = cu if cu_kv is None else torch.from_numpy(cu_kv).to(DEV)
+    s = torch.from_numpy(inp["sinks"]).to(DEV) if sinks else None
+    out, lse = amd.attn_sink_prefill(tbits(inp["q"]), tbits(inp["k"] if k is None else k),
+                                     tbits(inp["v"] if v is None else v), s, cu, cukv, inp["max_seqlen"],
+                                     inp["max_seqlen"] if max_kv is None else max_kv, spec.scale, spec.causal,
+                                     spec.window)
+    torch.cuda.synchronize()
+    return out_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_prefill(inp, spec, sinks=True, **kw):
+    s = inp["sinks"] if sinks else np.full_like(inp["sinks"], -np.inf)
+    return oracle.prefill_varlen(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), inp["cu_seqlens"], inp["cu_seqlens"], s,
+                                 spec.scale, spec.causal, spec.window, **kw)
+
+
+def test_tiny_causal_config(amd):
+    spec = CONFIGS["tiny_causal"]
+    inp = make_varlen(spec)
+    out, lse = run_prefill(amd, inp, spec)
+    ro, rl = oracle_prefill(inp, spec)
+    assert_close(out, lse, ro, rl, "tiny")
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (8, 8), (12, 2), (32, 2), (4, 4)])
+@pytest.mark.parametrize("window", [0, 128, 37])
+def test_prefill_ragged_causal(amd, hq, hkv, window):
+    spec = scaled(CONFIGS["causal_prefill"], batch=3, seqlen=(1, 300), hq=hq, hkv=hkv, window=window, seed=40 + hq)
+    inp = make_varlen(spec, seqlens=[300, 129, 1])
+    out, lse = run_prefill(amd, inp, spec)
+    ro, rl = oracle_prefill(inp, spec)
+    assert_close(out, lse, ro, rl, f"prefill G={hq // hkv} W={window}")
+
+
+@pytest.mark.parametrize("sinks", [False, True])
+def test_embedding_bidirectional_ragged(amd, sinks):
+    spec = scaled(CONFIGS["embed_sink"], batch=24, hq=4, hkv=4, seed=41)
+    inp = make_varlen(spec)
+    out, lse = run_prefill(amd, inp, spec, sinks=sinks)
+    ro, rl = oracle_prefill(inp, spec, sinks=sinks)
+    assert_close(out, lse, ro, rl, f"embed sinks={sinks}")
+
+
+def test_prefill_edge_cases(amd):
+    # empty sequences in the batch, a 1-token sequence, a sequence not a multiple of the tile
+    spec = scaled(CONFIGS["causal_prefill"], batch=5, hq=8, hkv=2, seed=42)
+    inp = make_varlen(spec, seqlens=[0, 65, 0, 1, 200])
+    out, lse = run_prefill(amd, inp, spec)
+    ro, rl = oracle_prefill(inp, spec)
+    assert_close(out, lse, ro, rl, "prefill edges")
+    # sinks pointer NULL == every sink disabled
+    out2, lse2 = run_prefill(amd, inp, spec, sinks=False)
+    ro2, rl2 = oracle_prefill(inp, spec, sinks=False)
+    assert_close(out2, lse2, ro2, rl2, "prefill no sinks")
+
+
+def test_prefill_mixed_and_extreme_sinks(amd):
+    spec = scaled(CONFIGS["causal_prefill"], batch=2, hq=8, hkv=1, seed=43)
+    inp = make_varlen(spec, seqlens=[40, 150])
+    inp["sinks"] = np.array([-np.inf, 0.0, 20.0, -20.0, 3.0, -np.inf, 8.0, 1.0], dtype=np.float32)
+    out, lse = run_prefill(amd, inp, spec)
+    ro, rl = oracle_prefill(inp, spec)
+    assert_close(out, lse, ro, rl, "extreme sinks")
+
+
+def test_prefill_queries_shorter_than_keys(amd):
+    """Chunked-prefill shape: the last Lq tokens attend to Lk >= Lq keys (bottom-right causal)."""
+    spec = scaled(CONFIGS["causal_prefill"], batch=2, hq=8, hkv=2, seed=44)
+    inp = make_varlen(spec, seqlens=[70, 33])
+    rng = np.random.default_rng(7)
+    lk = np.array([200, 33])
+    cu_kv = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    from workloads import bf16_round_bits
+    k = bf16_round_bits(rng.standard_normal((int(lk.sum()), 2, 64), dtype=np.float32))
+    v = bf16_round_bits(rng.standard_normal((int(lk.sum()), 2, 64), dtype=np.float32))
+    out, lse = run_prefill(amd, inp, spec, cu_kv=cu_kv, k=k, v=v, max_kv=200)
+    ro, rl = oracle.prefill_varlen(f64(inp["q"]), f64(k), f64(v), inp["cu_seqlens"], cu_kv, inp["sinks"], spec.scale,
+                                   True, 0)
+    assert_close(out, lse, ro, rl, "q shorter than kv")
+
+
+def test_prefill_deterministic(amd):
+    spec = scaled(CONFIGS["causal_prefill"], batch=2, hq=16, hkv=2, seed=45)
+    inp = make_varlen(spec, seqlens=[257, 300])
+    a = run_prefill(amd, inp, spec)
+    b = run_prefill(amd, inp, spec)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name", ["causal_prefill", "window_prefill"])
+def test_prefill_full_size_sampled(amd, name):
+    spec = CONFIGS[name]
+    inp = make_varlen(spec)
+    out, lse = run_prefill(amd, inp, spec)
+    rows = {0: [0, 1, 63, 64, 127, 128, 4095], 5: [2047, 4000], 7: [100, 3071, 4094]}
+    ro, rl = oracle_prefill(inp, spec, seqs=list(rows), rows=rows)
+    assert_close(out, lse, ro, rl, name)
+
+
+@pytest.mark.parametrize("name", ["embed_nosink", "embed_sink"])
+def test_embedding_full_size_sampled(amd, name):
+    spec = CONFIGS[name]
+    inp = make_varlen(spec)
+    out, lse = run_prefill(amd, inp, spec, sinks=spec.sink_std is not None)
+    ro, rl = oracle.prefill_varlen(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), inp["cu_seqlens"],
+                                   inp["cu_seqlens"], inp["sinks"], spec.scale, False, 0, seqs=[0, 1, 77, 300, 511])
+    assert_close(out, lse, ro, rl, name)
+
+
+# -------------------------------------------------------------------------------------------
+# paged decode / verify
+# -------------------------------------------------------------------------------------------
+def dev_paged(inp):
+    return dict(q=tbits(inp["q"]), k=tbits(inp["k_cache"]), v=tbits(inp["v_cache"]),
+                table=torch.from_numpy(inp["page_table"]).to(DEV), lens=torch.from_numpy(inp["kv_lens"]).to(DEV),
+                sinks=torch.from_numpy(inp["sinks"]).to(DEV))
+
+
+def run_decode(amd, d, inp, spec, chunk=None, workspace=None, sinks=True):
+    out, lse = amd.attn_sink_decode_paged(d["q"], d["k"], d["v"], d["table"], d["lens"], d["sinks"] if sinks else None,
+                                          spec.q_len, inp["max_kv_len"], spec.scale, spec.causal, spec.window,
+                                          spec.kv_chunk if chunk is None else chunk, workspace=workspace)
+    torch.cuda.synchronize()
+    return out_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_decode(inp, spec, seqs=None, sinks=True):
+    s = inp["sinks"] if sinks else np.full_like(inp["sinks"], -np.inf)
+    return oracle.decode_paged(f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"]), inp["page_table"],
+                               inp["kv_lens"], s, spec.q_len, spec.scale, spec.causal, spec.window, seqs=seqs)
+
+
+@pytest.mark.parametrize("q_len,hq,hkv", [(1, 16, 2), (1, 64, 8), (5, 16, 2), (2, 8, 1), (8, 64, 8), (3, 4, 4),
+                                          (1, 64, 1)])
+def test_decode_small(amd, q_len, hq, hkv):
+    spec = scaled(CONFIGS["verify"], batch=5, q_len=q_len, kv_len=(1, 1500), hq=hq, hkv=hkv, seed=50 + q_len + hq)
+    inp = make_paged(spec, kv_lens=[1500, 513, 512, 17, 8 if q_len <= 8 else q_len])
+    out, lse = run_decode(amd, dev_paged(inp), inp, spec)
+    ro, rl = oracle_decode(inp, spec)
+    assert_close(out, lse, ro, rl, f"decode q_len={q_len} G={hq // hkv}")
+
+
+@pytest.mark.parametrize("window", [1, 100, 600])
+def test_decode_window(amd, window):
+    spec = scaled(CONFIGS["verify"], batch=4, kv_len=(1, 2000), hq=16, hkv=2, window=window, seed=60)
+    inp = make_paged(spec)
+    out, lse = run_decode(amd, dev_paged(inp), inp, spec)
+    ro, rl = oracle_decode(inp, spec)
+    assert_close(out, lse, ro, rl, f"decode window {window}")
+
+
+def test_decode_edge_lengths_and_no_sink(amd):
+    spec = scaled(CONFIGS["verify"], batch=5, kv_len=(0, 700), hq=16, hkv=2, seed=61)
+    inp = make_paged(spec, kv_lens=[0, 3, 5, 700, 16], max_pages_per_seq=44)
+    d = dev_paged(inp)
+    for sinks in (True, False):
+        out, lse = run_decode(amd, d, inp, spec, sinks=sinks)
+        ro, rl = oracle_decode(inp, spec, sinks=sinks)
+        assert_close(out, lse, ro, rl, f"decode edges sinks={sinks}")
+
+
+@pytest.mark.parametrize("page_size,chunk", [(32, 512), (64, 256), (256, 512), (16, 64), (16, 0)])
+def test_decode_page_and_chunk_sizes(amd, page_size, chunk):
+    spec = scaled(CONFIGS["verify"], batch=4, q_len=2, kv_len=(100, 1300), hq=16, hkv=2, page_size=page_size,
+                  kv_chunk=chunk, seed=62)
+    inp = make_paged(spec)
+    out, lse = run_decode(amd, dev_paged(inp), inp, spec)
+    ro, rl = oracle_decode(inp, spec)
+    assert_close(out, lse, ro, rl, f"page {page_size} chunk {chunk}")
+
+
+def test_decode_plan_is_bit_exact_and_partials_match(amd):
+    spec = scaled(CONFIGS["verify"], batch=6, kv_len=(1, 1800), hq=16, hkv=2, seed=63)
+    inp = make_paged(spec, kv_lens=[1800, 1, 512, 513, 0, 1024])
+    d = dev_paged(inp)
+    need = amd.attn_sink_decode_workspace_size(6, spec.q_len, inp["max_kv_len"], spec.hq, 64, spec.kv_chunk)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    run_decode(amd, d, inp, spec, workspace=ws)
+    lay = amd.decode_workspace_layout(6, spec.q_len, inp["max_kv_len"], spec.hq, spec.kv_chunk)
+    w = ws.cpu().numpy()
+    rows = lay["rows"]
+    indptr = w[:4 * (rows + 1)].view(np.int32)
+    counts = w[lay["off_counts"]:lay["off_counts"] + 4 * rows].view(np.int32)
+    exp_counts, exp_indptr = oracle.plan_chunks(inp["kv_lens"], spec.q_len, spec.kv_chunk)
+    assert counts.tolist() == exp_counts and indptr.tolist() == exp_indptr
+    n = exp_indptr[-1]
+    o_p = w[lay["off_o"]:lay["off_o"] + 4 * n * spec.hq * 64].view(np.float32).reshape(n, spec.hq, 64)
+    l_p = w[lay["off_lse"]:lay["off_lse"] + 4 * n * spec.hq].view(np.float32).reshape(n, spec.hq)
+    ro_p, rl_p, _, _ = oracle.split_decode(f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"]),
+                                           inp["page_table"], inp["kv_lens"], inp["sinks"], spec.q_len, spec.scale,
+                                           spec.kv_chunk)
+    assert_close(o_p.astype(np.float64), l_p.astype(np.float64), ro_p, rl_p, "partials")
+
+
+def test_merge_kernel_on_oracle_partials(amd):
+    spec = scaled(CONFIGS["verify"], batch=4, kv_len=(1, 1600), hq=8, hkv=2, seed=64)
+    inp = make_paged(spec, kv_lens=[1600, 2, 700, 0])
+    o_p, l_p, counts, indptr = oracle.split_decode(f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"]),
+                                                   inp["page_table"], inp["kv_lens"], inp["sinks"], spec.q_len,
+                                                   spec.scale, 256)
+    out, lse = amd.attn_sink_merge_partials(torch.from_numpy(o_p.astype(np.float32)).to(DEV),
+                                            torch.from_numpy(l_p.astype(np.float32)).to(DEV),
+                                            torch.tensor(indptr, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(inp, spec)
+    assert_close(out_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, "merge on oracle partials")
+
+
+def test_merge_all_empty_rows(amd):
+    o = torch.ones(3, 4, 64, device=DEV)
+    l = torch.full((3, 4), float("-inf"), device=DEV)
+    indptr = torch.tensor([0, 2, 2, 3], dtype=torch.int32, device=DEV)
+    out, lse = amd.attn_sink_merge_partials(o, l, indptr)
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_page_permutation_bit_identical(amd):
+    spec = scaled(CONFIGS["verify"], batch=4, kv_len=(50, 1200), hq=16, hkv=2, seed=65)
+    inp = make_paged(spec)
+    a = run_decode(amd, dev_paged(inp), inp, spec)
+    perm = np.random.default_rng(3).permutation(inp["num_pages"])
+    inv = np.argsort(perm)
+    inp2 = dict(inp)
+    inp2["k_cache"], inp2["v_cache"] = inp["k_cache"][inv], inp["v_cache"][inv]
+    inp2["page_table"] = perm[inp["page_table"]].astype(np.int32)
+    b = run_decode(amd, dev_paged(inp2), inp2, spec)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_chunk_size_invariance(amd):
+    spec = scaled(CONFIGS["paged_decode"], batch=4, kv_len=(1000, 5000), hq=16, hkv=2, seed=66)
+    inp = make_paged(spec)
+    d = dev_paged(inp)
+    ro, rl = oracle_decode(inp, spec)
+    for chunk in (128, 512, 2048, 0):
+        out, lse = run_decode(amd, d, inp, spec, chunk=chunk)
+        assert_close(out, lse, ro, rl, f"chunk {chunk}")
+
+
+def test_gqa_matches_repeated_mha(amd):
+    spec = scaled(CONFIGS["paged_decode"], batch=3, kv_len=(100, 900), hq=16, hkv=2, seed=67)
+    inp = make_paged(spec)
+    a = run_decode(amd, dev_paged(inp), inp, spec)
+    inp2 = dict(inp)
+    inp2["k_cache"] = np.repeat(inp["k_cache"], 8, axis=1)
+    inp2["v_cache"] = np.repeat(inp["v_cache"], 8, axis=1)
+    b = run_decode(amd, dev_paged(inp2), inp2, scaled(spec, hkv=16))
+    assert np.abs(a[0] - b[0]).max() <= 2e-2 and np.abs(a[1] - b[1]).max() <= 1e-4
+
+
+def test_decode_deterministic(amd):
+    spec = scaled(CONFIGS["verify"], batch=3, kv_len=(100, 2000), hq=64, hkv=8, seed=68)
+    inp = make_paged(spec)
+    d = dev_paged(inp)
+    a = run_decode(amd, d, inp, spec)
+    b = run_decode(amd, d, inp, spec)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name", ["paged_decode", "verify"])
+def test_decode_full_size(amd, name):
+    spec = CONFIGS[name]
+    inp = make_paged(spec)
+    out, lse = run_decode(amd, dev_paged(inp), inp, spec)
+    seqs = list(range(spec.batch)) if name == "paged_decode" else [0, 1, 7, 19, 31]
+    ro, rl = oracle_decode(inp, spec, seqs=seqs)
+    assert_close(out, lse, ro, rl, name)
