@@ -1,0 +1,332 @@
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+Default workload: paged split-KV decode (64 sequences, q_len 1, KV lengths uniform in
+[1024, 8192], 64 query / 8 KV heads, head_dim 64, bf16, 16-token pages in a seeded random
+order, 512-token chunks merged by log-sum-exp). One step = one attn_sink_decode_paged call
+(split-KV kernel + merge kernel) over the whole batch, inputs resident in HBM.
+
+Other workloads (--workload): causal_prefill, window_prefill, verify, embed (two passes:
+sinks disabled, then N(0,1) sinks), tiny_causal.
+
+Prints ONE JSON line. ``value`` is the algorithmic rate of the whole step (GB/s for the
+memory-bound paths, TFLOP/s for prefill); ``roofline`` describes the dominant kernel, timed
+with HIP events on the stream it runs on; ``cpu_baseline`` times the fp64 CPU oracle on a
+bounded sample of the same workload (rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_varlen  # noqa: E402
+
+METRIC = "sink-attn decode HBM GB/s (% peak); prefill TFLOP/s (% bf16 MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "common.hpp", "kernels.hpp"],
+    "prefill": ["prefill.hip", "common.hpp", "kernels.hpp"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="paged_decode",
+                    choices=["paged_decode", "verify", "causal_prefill", "window_prefill", "embed", "tiny_causal"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU oracle sample (wall seconds)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+def tbits(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def source_hash(kind):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "gqa_attention_sinks_sink_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, kind):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    rec = data.get(name)
+    if rec is None or rec.get("source_hash") != source_hash(kind):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_calls(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def cold_time(torch, fn, steps, scratch):
+    """Median per-call time with a 1 GiB write before each call (L2 and MALL flushed)."""
+    ts = []
+    for _ in range(steps):
+        scratch.fill_(1)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e))
+    return float(np.median(ts))
+
+
+# ------------------------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+# ------------------------------------------------------------------------------------------
+def cpu_baseline_paged(inp, spec, seconds, bytes_per_seq):
+    import oracle
+    from threadpoolctl import threadpool_limits
+    f64 = lambda b: bf16_bits_to_f32(b).astype(np.float64)
+    q, kc, vc = f64(inp["q"]), inp["k_cache"], inp["v_cache"]
+    done_bytes, n = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < seconds:
+            b = n % spec.batch
+            L = int(inp["kv_lens"][b])
+            pages = inp["page_table"][b, :(L + spec.page_size - 1) // spec.page_size]
+            # the oracle reads only this sequence's pages; pass it a compact pool of them
+            sub_k = f64(kc[pages])
+            sub_v = f64(vc[pages])
+            table = np.arange(len(pages), dtype=np.int32)[None, :]
+            oracle.decode_paged(q[b * spec.q_len:(b + 1) * spec.q_len], sub_k, sub_v, table,
+                                np.array([L], dtype=np.int32), inp["sinks"], spec.q_len, spec.scale, spec.causal,
+                                spec.window)
+            done_bytes += bytes_per_seq[b]
+            n += 1
+    dt = time.perf_counter() - t0
+    return done_bytes / dt / 1e9, n, dt
+
+
+def cpu_baseline_varlen(inp, spec, seconds, flops_per_seq, sinks):
+    import oracle
+    from threadpoolctl import threadpool_limits
+    f64 = lambda b: bf16_bits_to_f32(b).astype(np.float64)
+    cu = inp["cu_seqlens"]
+    done, n = 0.0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < seconds:
+            b = n % len(flops_per_seq)
+            s0, s1 = int(cu[b]), int(cu[b + 1])
+            sub_cu = np.array([0, s1 - s0], dtype=np.int32)
+            oracle.prefill_varlen(f64(inp["q"][s0:s1]), f64(inp["k"][s0:s1]), f64(inp["v"][s0:s1]), sub_cu, sub_cu,
+                                  sinks, spec.scale, spec.causal, spec.window)
+            done += flops_per_seq[b]
+            n += 1
+    dt = time.perf_counter() - t0
+    return done / dt / 1e12, n, dt
+
+
+# ------------------------------------------------------------------------------------------
+def pairs_visible(L, causal, window):
+    L = np.asarray(L, dtype=np.int64)
+    if not causal:
+        return L * L if window <= 0 else None
+    if window <= 0:
+        return L * (L + 1) // 2
+    W = window
+    full = np.minimum(L, W)
+    return full * (full + 1) // 2 + np.maximum(L - W, 0) * W
+
+
+def bench_paged(args, torch, amd, name):
+    spec = CONFIGS[name]
+    inp = make_paged(spec)
+    dev = torch.device("cuda:0")
+    q = tbits(torch, inp["q"], dev)
+    kc = tbits(torch, inp["k_cache"], dev)
+    vc = tbits(torch, inp["v_cache"], dev)
+    table = torch.from_numpy(inp["page_table"]).to(dev)
+    lens = torch.from_numpy(inp["kv_lens"]).to(dev)
+    sinks = torch.from_numpy(inp["sinks"]).to(dev)
+    B, ql, hq, hkv = spec.batch, spec.q_len, spec.hq, spec.hkv
+    need = amd.attn_sink_decode_workspace_size(B, ql, inp["max_kv_len"], hq, 64, spec.kv_chunk)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((B * ql, hq), dtype=torch.float32, device=dev)
+
+    def step():
+        amd.attn_sink_decode_paged(q, kc, vc, table, lens, sinks, ql, inp["max_kv_len"], spec.scale, spec.causal,
+                                   spec.window, spec.kv_chunk, workspace=ws, out=out, lse=lse)
+
+    L = inp["kv_lens"].astype(np.int64)
+    kv_bytes_seq = L * hkv * 64 * 2 * 2
+    pages_seq = (L + spec.page_size - 1) // spec.page_size
+    q_bytes = B * ql * hq * 64 * 2
+    algo_bytes = int(kv_bytes_seq.sum() + q_bytes * 2 + B * ql * hq * 4 + pages_seq.sum() * 4 + B * 4 + hq * 4)
+    kernel_bytes = int(kv_bytes_seq.sum() + q_bytes + pages_seq.sum() * 4)   # split-KV kernel, per launch
+    flops = int((L * hkv).sum() * (hq // hkv) * ql * 4 * 64)
+
+    ms = time_calls(torch, step, args.steps, args.warmup)
+    # merge kernel alone on the same partials -> split-KV kernel time = call - merge
+    lay = amd.decode_workspace_layout(B, ql, inp["max_kv_len"], hq, spec.kv_chunk, spec.page_size)
+    n_p = lay["partials"]
+    o_p = ws[lay["off_o"]:lay["off_o"] + 4 * n_p * hq * 64].view(torch.float32).view(n_p, hq, 64)
+    l_p = ws[lay["off_lse"]:lay["off_lse"] + 4 * n_p * hq].view(torch.float32).view(n_p, hq)
+    indptr = ws[:4 * (lay["rows"] + 1)].view(torch.int32)
+    out2 = torch.empty_like(out)
+    merge_ms = time_calls(torch, lambda: amd.attn_sink_merge_partials(o_p, l_p, indptr, out=out2, return_lse=False),
+                          args.steps, args.warmup)
+    split_ms = max(ms - merge_ms, 1e-6)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold_ms = cold_time(torch, step, max(5, min(args.steps, 20)), scratch)
+    del scratch
+
+    value = algo_bytes / (ms * 1e-3) / 1e9
+    achieved = kernel_bytes / (split_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: {B} seqs x q_len {ql}, kv {spec.kv_len[0]}..{spec.kv_len[1]} "
+                               f"(sum {int(L.sum())}), {hq}/{hkv} heads, d 64, {spec.page_size}-token pages, "
+                               f"{spec.kv_chunk}-token chunks, sinks N(0,{spec.sink_std}^2)",
+                   "algorithmic_bytes": algo_bytes, "algorithmic_flops": flops},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"kernel": "decode_split_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(name, "decode"), "algorithmic_bytes_per_launch": kernel_bytes,
+                     "kernel_ms": round(split_ms, 5), "merge_ms": round(merge_ms, 5)},
+        "cold_l2_mall_ms_per_step": round(cold_ms, 5),
+        "cold_value": round(algo_bytes / (cold_ms * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        v, n, dt = cpu_baseline_paged(inp, spec, args.cpu_seconds, kv_bytes_seq)
+        res["cpu_baseline"] = {"value": round(v, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} sequences of this batch (cycled from sequence 0), {dt:.1f} s wall, "
+                                         f"fp64 NumPy, BLAS limited to 1 thread"}
+    return res
+
+
+def bench_varlen(args, torch, amd, name):
+    if name == "embed":
+        specs = [CONFIGS["embed_nosink"], CONFIGS["embed_sink"]]
+    else:
+        specs = [CONFIGS[name]]
+    spec = specs[-1]
+    inp = make_varlen(spec)
+    dev = torch.device("cuda:0")
+    q, k, v = (tbits(torch, inp[x], dev) for x in ("q", "k", "v"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+    sinks = torch.from_numpy(inp["sinks"]).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], spec.hq), dtype=torch.float32, device=dev)
+    mx = inp["max_seqlen"]
+
+    def one(s, use_sinks):
+        amd.attn_sink_prefill(q, k, v, sinks if use_sinks else None, cu, cu, mx, mx, s.scale, s.causal, s.window,
+                              out=out, lse=lse)
+
+    def step():
+        for s in specs:
+            one(s, s.sink_std is not None)
+
+    lens = inp["seqlens"].astype(np.int64)
+    pairs = pairs_visible(lens, spec.causal, spec.window)
+    flops_seq = pairs * 4 * 64 * spec.hq
+    flops = int(flops_seq.sum()) * len(specs)
+    T = int(lens.sum())
+    io_bytes = T * (spec.hq * 64 * 2 * 2 + spec.hkv * 64 * 2 * 2 + spec.hq * 4)
+    algo_bytes = io_bytes * len(specs)
+
+    ms = time_calls(torch, step, args.steps, args.warmup)
+    kernel_ms = ms / len(specs)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    ai = flops / algo_bytes
+    bound = "mfma" if ai > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm"
+    if bound == "mfma":
+        roof = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(flops / len(specs) / (kernel_ms * 1e-3) / 1e12, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": "prefill_kernel", "bound": "hbm", "achieved": round(io_bytes / (kernel_ms * 1e-3) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = measured_traffic(name, "prefill")
+    roof["algorithmic_flops_per_launch"] = int(flops_seq.sum())
+    roof["algorithmic_bytes_per_launch"] = io_bytes
+    roof["kernel_ms"] = round(kernel_ms, 5)
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: {spec.batch} seqs, lengths {spec.seqlen[0]}..{spec.seqlen[1]} (sum {T}), "
+                               f"{spec.hq}/{spec.hkv} heads, d 64, causal={spec.causal}, window={spec.window}, "
+                               f"passes={len(specs)}",
+                   "algorithmic_flops": flops, "algorithmic_bytes": algo_bytes},
+        "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2), "gb_per_s": round(gbs, 1),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        s = inp["sinks"] if spec.sink_std is not None else np.full(spec.hq, -np.inf, dtype=np.float32)
+        v, n, dt = cpu_baseline_varlen(inp, spec, args.cpu_seconds, flops_seq, s)
+        res["cpu_baseline"] = {"value": round(v, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} sequences of this batch (cycled from sequence 0), {dt:.1f} s wall, "
+                                         f"fp64 NumPy, BLAS limited to 1 thread"}
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this build measures the "
+              f"one-GPU shard of the path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (HIP device)", file=sys.stderr)
+        sys.exit(1)
+    import gqa_attention_sinks_sink_amd as amd
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(3)
+        for _ in range(3):
+            b = a.clone()
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30}))
+        return
+    if args.workload in ("paged_decode", "verify"):
+        res = bench_paged(args, torch, amd, args.workload)
+    else:
+        res = bench_varlen(args, torch, amd, args.workload)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

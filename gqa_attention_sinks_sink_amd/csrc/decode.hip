@@ -262,7 +262,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   }
   __syncthreads();  // also: every wave is done with its V staging area
   float* obuf = reinterpret_cast<float*>(lds);  // [NT*16 columns][64 d] fp32, reuses V staging
-  for (int i = threadIdx.x; i < NT * 16 * kHeadDim; i += kThreads) obuf[i] = 0.f;
   float mtot[NT], ltot[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -277,21 +276,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     mtot[nt] = M;
     ltot[nt] = Lt;
   }
-  __syncthreads();
+  // Waves add their rescaled O^T into the buffer one after another (fixed order, so the
+  // result is bit-reproducible).
+  float f[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int col = nt * 16 + col_lo;
     const float Mu = (mtot[nt] == kNegInf) ? 0.f : mtot[nt];
-    const float f = (ltot[nt] > 0.f) ? fast_exp2(m[nt] - Mu) / ltot[nt] : 0.f;
+    f[nt] = (ltot[nt] > 0.f) ? fast_exp2(m[nt] - Mu) / ltot[nt] : 0.f;
+  }
+  for (int ww = 0; ww < kWaves; ++ww) {
+    if (w == ww) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = nt * 16 + col_lo;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        atomicAdd(&obuf[col * kHeadDim + dt * 16 + grp * 4 + i], o[nt][dt][i] * f);
+        for (int dt = 0; dt < 4; ++dt) {
+          f32x4* dst = reinterpret_cast<f32x4*>(&obuf[col * kHeadDim + dt * 16 + grp * 4]);
+          const f32x4 add = o[nt][dt] * f[nt];
+          *dst = (ww == 0) ? add : (*dst + add);
+        }
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- write the partial: o_c (normalised), lse_c (natural log)
   for (int i = threadIdx.x; i < R * (kHeadDim / 4); i += kThreads) {
