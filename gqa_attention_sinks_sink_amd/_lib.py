@@ -15,7 +15,7 @@ from typing import Optional, Tuple
 
 import torch
 
-from .build import LIB_PATH
+from .build import LIB_LOAD_PATH as LIB_PATH
 
 __all__ = [
     "lib", "AttnSinkError", "attn_sink_prefill", "attn_sink_decode_paged", "attn_sink_decode_workspace_size",

@@ -18,6 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libattnsink.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+# Developer override: load a library built elsewhere (e.g. an experimental variant).
+LIB_LOAD_PATH = os.environ.get("ATTN_SINK_LIB", LIB_PATH)
 SOURCES = ["api.hip", "prefill.hip", "decode.hip", "merge.hip"]
 ARCH = "gfx950"
 
@@ -33,6 +35,9 @@ def compile_flags() -> list:
         f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
         # packed FP32 instructions stay off: plain fp32 code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep MFMA accumulators in VGPRs: the softmax reads every score tile with VALU ops,
+        # and AGPR-resident results would be copied back and forth on every tile
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", os.path.join(ROOT, "include"), "-Wno-unused-result",
     ]
 

@@ -150,7 +150,7 @@ attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, cons
   if (chunk > INT32_MAX / 2) return ATTN_SINK_ERR_UNSUPPORTED;
   DecodeLayout lay;
   if (!decode_layout(batch, q_len, max_kv_len, num_q_heads, chunk, &lay)) return ATTN_SINK_ERR_UNSUPPORTED;
-  if (lay.chunks * batch > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (lay.chunks * batch * num_kv_heads > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
   if (batch == 0) return ATTN_SINK_OK;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || page_table == nullptr || kv_lens == nullptr ||
       out == nullptr || workspace == nullptr)
@@ -207,7 +207,6 @@ attn_sink_status attn_sink_merge_partials(const float* o_partial, const float* l
                                           int32_t head_dim, void* out, float* lse, void* stream) {
   if (num_partials < 0 || num_rows < 0 || num_q_heads <= 0) return ATTN_SINK_ERR_INVALID_ARG;
   if (head_dim != kSupportedHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
-  if ((num_q_heads + 3) / 4 > kMaxGridY) return ATTN_SINK_ERR_UNSUPPORTED;
   if (num_rows == 0) return ATTN_SINK_OK;
   if (partial_indptr == nullptr || out == nullptr) return ATTN_SINK_ERR_INVALID_ARG;
   if (num_partials > 0 && (o_partial == nullptr || lse_partial == nullptr)) return ATTN_SINK_ERR_INVALID_ARG;

@@ -65,6 +65,12 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* lds_addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, const_cast<void*>(lds_addr)));
 }
 
+// Two transposing reads (keys k0..k0+3 and the next 4 keys) as one 8-element MFMA operand.
+__device__ __forceinline__ u32x4 join_tr16(s16x4 lo, s16x4 hi) {
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }

@@ -4,18 +4,28 @@
 // scores plus one sink logit per head; computed online with a running maximum m and a
 // scale d; the running maximum of the first KV chunk is seeded with the head's sink
 // (d = 1), later chunks start from m = -inf; chunk partials are merged by log-sum-exp
-// (merge.hip).
+// (merge.hip). Heads and the KV length are processed in parallel (same section).
 //
-// Work decomposition (one workgroup = one sequence x one KV head x one KV chunk):
-//   * columns = the q_len query tokens x G query heads that share the KV head
-//     (GQA: one K/V fetch serves all of them), padded to NT tiles of 16;
-//   * 4 waves split the chunk's keys; each wave streams 32 keys (two 16-key groups)
-//     per step straight from HBM into registers in the MFMA operand layout;
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys x columns), masks from indices,
-//     online softmax in the exp2 domain, O^T += V^T P^T with V transposed on its way
-//     out of LDS by ds_read_b64_tr_b16;
-//   * the 4 wave states are combined in LDS and the chunk partial (o/d, m + ln d) is
-//     written to the workspace at the plan's offset.
+// Work decomposition
+//   * A work item is (sequence b, KV chunk c, KV head g). Items are enumerated densely
+//     over the chunks that exist (n_b = max(1, ceil(L_b / chunk)) per sequence), with the
+//     KV head varying fastest so that the workgroups running side by side read all heads'
+//     blocks of the same pages (one page of all heads is contiguous in HBM).
+//   * The kernel is persistent: a grid sized to fill the chip walks the item list with a
+//     stride of gridDim.x. Each workgroup finds the sequence of an item with a running
+//     prefix-sum cursor over kv_lens (64 sequences per wave-wide step), so no host-side
+//     plan and no per-item search table are needed, and the grid depends only on host
+//     scalars.
+//   * Inside an item, columns = the q_len query tokens x G query heads that share the KV
+//     head (one K/V fetch serves all of them), padded to NT tiles of 16. The chunk's keys
+//     are cut into 32-key steps dealt round-robin to the 4 waves; a step is two 16-key
+//     groups, each inside one page.
+//   * Per step: K goes from HBM straight into registers in the MFMA A layout; S^T = K Q^T
+//     with v_mfma_f32_16x16x32_bf16; masks from indices; online softmax in the exp2
+//     domain; V rows pass through LDS and come back transposed (ds_read_b64_tr_b16) as
+//     the A operand of O^T += V^T P^T.
+//   * The 4 wave states are combined in LDS in a fixed order (bit-reproducible) and the
+//     chunk partial (o/d, m + ln d) goes to the workspace at the plan's offset.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,6 +37,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kVRowBytes = 160;               // padded LDS row of V (64 bf16 = 128 B + 32)
 constexpr int kVWaveBytes = 32 * kVRowBytes;  // 32 keys per wave step
+constexpr int kSegKeys = 1024;                // keys whose page ids one wave holds (64 lanes x 16)
+constexpr float kLazyMax = 8.0f;              // running-max slack (log2 units) before a rescale
 
 __device__ __forceinline__ int seq_len_clamped(const DecodeParams& p, int b) {
   int L = p.kv_lens[b];
@@ -45,296 +57,429 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   return v;
 }
 
-// Byte offset of the K/V row (page, kv head, slot) in the cache.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+// Element offset of the K/V row (page, kv head, slot) in the cache.
 __device__ __forceinline__ size_t cache_row(const DecodeParams& p, int page, int kvh, int slot) {
   return (((size_t)page * p.hkv + kvh) * p.page_size + slot) * (size_t)kHeadDim;
 }
 
 }  // namespace
 
+// Minimum resident waves per SIMD requested per column-tile count. The kernel is bound by
+// memory latency, so register pressure is traded for waves in flight (measured on MI355X).
 template <int NT>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+struct DecodeOccupancy { static constexpr int value = 1; };
+template <> struct DecodeOccupancy<1> { static constexpr int value = 4; };
+template <> struct DecodeOccupancy<2> { static constexpr int value = 3; };
+template <> struct DecodeOccupancy<3> { static constexpr int value = 4; };
+template <> struct DecodeOccupancy<4> { static constexpr int value = 2; };
+
+template <int NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DecodeOccupancy<NT>::value, 8)))
+void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * kVWaveBytes];
   __shared__ float red_m[kWaves][NT * 16];
   __shared__ float red_l[kWaves][NT * 16];
 
-  const int max_chunks = gridDim.x / p.batch;
-  const int b = blockIdx.x / max_chunks;
-  const int c = blockIdx.x - b * max_chunks;
-  const int kvh = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-
-  const int L = seq_len_clamped(p, b);
-  const int n_b = chunks_for(L, p.kv_chunk);
-  if (c >= n_b) return;
-
-  // ---- plan: partial offset of this sequence (exclusive prefix over earlier sequences)
-  int acc = 0;
-  for (int i = lane; i < b; i += 64) acc += chunks_for(seq_len_clamped(p, i), p.kv_chunk);
-  const int base = wave_sum_int(acc) * p.q_len;  // indptr of row b*q_len
-  if (c == 0 && kvh == 0 && w == 0) {
-    if (lane < p.q_len) {
-      p.counts[b * p.q_len + lane] = n_b;
-      p.indptr[b * p.q_len + lane] = base + lane * n_b;
-    }
-    if (b == p.batch - 1 && lane == 0) p.indptr[p.batch * p.q_len] = base + p.q_len * n_b;
-  }
-
   const int G = p.group;
   const int R = p.q_len * G;  // live columns
   const int col_lo = lane & 15;
   const int grp = lane >> 4;  // 16-lane group 0..3
-
-  // ---- Q^T as the B operand (k = head dim), one 16-column tile per nt
-  u32x4 qb[NT][2];
-  int pos[NT];  // absolute position of each lane's column (for masks)
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int col = nt * 16 + col_lo;
-    const int t = col / G, gh = col - (col / G) * G;
-    pos[nt] = L - p.q_len + t;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (col < R) {
-        const size_t off = ((size_t)(b * p.q_len + t) * p.hq + kvh * G + gh) * kHeadDim + ks * 32 + grp * 8;
-        qb[nt][ks] = *reinterpret_cast<const u32x4*>(p.q + off);
-      } else {
-        qb[nt][ks] = u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-
-  // ---- online-softmax state per lane: m (exp2 domain, same across the 4 lane groups of a
-  // column), a partial row sum, and O^T tiles (d = dt*16 + 4*grp + i, column nt*16 + col_lo).
-  float m[NT], lsum[NT];
-  f32x4 o[NT][4];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int col = nt * 16 + col_lo;
-    const int h = kvh * G + (col < R ? col % G : 0);
-    // First chunk: the running max starts at the head's sink and d at 1 (held by lane group 0
-    // so the column sum counts it once). Other chunks and waves: m = -inf (d = 1 is inert).
-    const float sink2 = (p.sinks != nullptr) ? p.sinks[h] * kLog2e : kNegInf;
-    m[nt] = (c == 0 && w == 0) ? sink2 : kNegInf;
-    lsum[nt] = (grp == 0) ? 1.0f : 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[nt][dt] = f32x4{0, 0, 0, 0};
-  }
-
-  // ---- this wave's key range inside the chunk
-  const int chunk_lo = c * p.kv_chunk;
-  const int chunk_hi = min(chunk_lo + p.kv_chunk, L);
-  const int per_wave = p.kv_chunk / kWaves;  // multiple of 16
-  const int w_lo = chunk_lo + w * per_wave;
-  const int w_hi = min(w_lo + per_wave, chunk_hi);
   unsigned char* vl = lds + w * kVWaveBytes;
-  const int* ptab = p.page_table + (size_t)b * p.max_pages;
 
-  // Address of 16-key group starting at key j (group lies inside one page: page_size % 16 == 0).
-  auto group_row = [&](int j) -> size_t {
-    int pg = ptab[j >> p.page_shift];
-    pg = clampi(pg, 0, p.num_pages - 1);
-    return cache_row(p, pg, kvh, j & (p.page_size - 1));
+  // ---- total number of (sequence, chunk) pairs, and a cursor over sequences
+  int tot = 0;
+  for (int i = lane; i < p.batch; i += 64) tot += chunks_for(seq_len_clamped(p, i), p.kv_chunk);
+  const int total_items = wave_sum_int(tot) * p.hkv;
+
+  int cur_base = 0;    // first sequence of the cursor window
+  int cur_before = 0;  // pairs before cur_base
+  int win_incl = 0;    // inclusive prefix of chunk counts inside the window (this lane's sequence)
+  int win_total = 0;
+  auto load_window = [&]() {
+    const int i = cur_base + lane;
+    const int n = (i < p.batch) ? chunks_for(seq_len_clamped(p, i), p.kv_chunk) : 0;
+    win_incl = wave_inclusive_scan(n, lane);
+    win_total = __builtin_amdgcn_readlane(win_incl, 63);
   };
+  load_window();
 
-  for (int j0 = w_lo; j0 < w_hi; j0 += 32) {
-    const bool hasB = (j0 + 16) < w_hi;
-    // K as the A operand: row = key (lane & 15), k = head dim slice.
-    u32x4 ka[2][2], vrow[4];
-    {
-      const size_t rA = group_row(j0);
-      const size_t rB = hasB ? group_row(j0 + 16) : rA;
+  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+    const int P = item / p.hkv;
+    const int kvh = item - P * p.hkv;
+    while (P >= cur_before + win_total) {
+      cur_before += win_total;
+      cur_base += 64;
+      load_window();
+    }
+    const unsigned long long before_mask = __ballot(cur_before + win_incl <= P);
+    const int idx = __popcll(before_mask);
+    const int b = cur_base + idx;
+    const int pairs_before = cur_before + (idx > 0 ? __builtin_amdgcn_readlane(win_incl, idx - 1) : 0);
+    const int c = P - pairs_before;
+
+    const int L = seq_len_clamped(p, b);
+    const int n_b = chunks_for(L, p.kv_chunk);
+    const int base = pairs_before * p.q_len;  // indptr of row b*q_len
+    const int chunk_lo = c * p.kv_chunk;
+    const int chunk_hi = min(chunk_lo + p.kv_chunk, L);
+    const int* ptab = p.page_table + (size_t)b * p.max_pages;
+
+    // Page ids of up to 64 16-key groups (one per lane) for a segment of <= 1024 keys.
+    auto load_page_ids = [&](int seg_lo, int seg_hi) -> int {
+      const int j = seg_lo + 16 * lane;
+      int pg = 0;
+      if (j < seg_hi) pg = clampi(ptab[j >> p.page_shift], 0, p.num_pages - 1);
+      return pg;
+    };
+    int pid = load_page_ids(chunk_lo, min(chunk_lo + kSegKeys, chunk_hi));
+
+    // ---- Q^T as the B operand (k = head dim), one 16-column tile per nt
+    u32x4 qb[NT][2];
+    int pos[NT];  // absolute position of each lane's column (for masks)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = nt * 16 + col_lo;
+      const int t = col / G, gh = col - (col / G) * G;
+      pos[nt] = L - p.q_len + t;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        ka[0][ks] = *reinterpret_cast<const u32x4*>(p.k_cache + rA + (size_t)col_lo * kHeadDim + ks * 32 + grp * 8);
-        ka[1][ks] = hasB ? *reinterpret_cast<const u32x4*>(p.k_cache + rB + (size_t)col_lo * kHeadDim + ks * 32 + grp * 8)
-                         : u32x4{0, 0, 0, 0};
-      }
-      // V rows for LDS: lane covers key (lane>>3) + 8*ii of the 32, 16 B chunk (lane & 7).
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int kr = (lane >> 3) + 8 * ii;  // 0..31
-        const int key = j0 + kr;
-        const size_t rr = (kr < 16) ? rA : rB;
-        if (key < w_hi) {
-          vrow[ii] = *reinterpret_cast<const u32x4*>(p.v_cache + rr + (size_t)(kr & 15) * kHeadDim + (lane & 7) * 8);
+        if (col < R) {
+          const size_t off = ((size_t)(b * p.q_len + t) * p.hq + kvh * G + gh) * kHeadDim + ks * 32 + grp * 8;
+          qb[nt][ks] = *reinterpret_cast<const u32x4*>(p.q + off);
         } else {
-          vrow[ii] = u32x4{0, 0, 0, 0};  // keys past the range contribute exact zeros
+          qb[nt][ks] = u32x4{0, 0, 0, 0};
         }
       }
     }
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int kr = (lane >> 3) + 8 * ii;
-      *reinterpret_cast<u32x4*>(vl + kr * kVRowBytes + (lane & 7) * 16) = vrow[ii];
-    }
 
-    // S^T tiles: 16 keys x 16 columns per (group, nt).
-    f32x4 s[NT][2];
+    // ---- keys visible to each column inside this chunk: [vis_lo, vis_hi); wave-wide bounds
+    // decide whether a step needs masking at all.
+    int vis_lo[NT], vis_hi[NT];
+    int hi_min = 0x7fffffff, lo_max = -0x7fffffff;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        f32x4 a = f32x4{0, 0, 0, 0};
-        a = mfma16(as_bf16x8(ka[g][0]), as_bf16x8(qb[nt][0]), a);
-        a = mfma16(as_bf16x8(ka[g][1]), as_bf16x8(qb[nt][1]), a);
-        s[nt][g] = a;
+      vis_hi[nt] = p.causal ? min(chunk_hi, pos[nt] + 1) : chunk_hi;
+      vis_lo[nt] = (p.window > 0) ? max(chunk_lo, pos[nt] - p.window + 1) : chunk_lo;
+      if (vis_hi[nt] < vis_lo[nt]) vis_hi[nt] = vis_lo[nt];
+      if (nt * 16 + col_lo < R) {
+        hi_min = min(hi_min, vis_hi[nt]);
+        lo_max = max(lo_max, vis_lo[nt]);
       }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      hi_min = min(hi_min, __shfl_xor(hi_min, off, 64));
+      lo_max = max(lo_max, __shfl_xor(lo_max, off, 64));
+    }
+    const int vis_hi_min = hi_min, vis_lo_max = lo_max;
 
-    // Masks + online softmax update per column tile.
-    bf16x8 pb[NT];
+    // ---- online-softmax state per lane: m (exp2 domain, same across the 4 lane groups of a
+    // column), a partial row sum, and O^T tiles (d = dt*16 + 4*grp + i, column nt*16 + col_lo).
+    float m[NT], lsum[NT];
+    f32x4 o[NT][4];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float mx = kNegInf;
+      const int col = nt * 16 + col_lo;
+      const int h = kvh * G + (col < R ? col % G : 0);
+      // First chunk: the running max starts at the head's sink and d at 1 (held by lane group
+      // 0 so the column sum counts it once). Other chunks and waves: m = -inf (d = 1 is inert).
+      const float sink2 = (p.sinks != nullptr) ? p.sinks[h] * kLog2e : kNegInf;
+      m[nt] = (c == 0 && w == 0) ? sink2 : kNegInf;
+      lsum[nt] = (grp == 0) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = j0 + g * 16 + grp * 4 + i;
-          bool ok = key < w_hi;
-          if (p.causal) ok = ok && key <= pos[nt];
-          if (p.window > 0) ok = ok && (pos[nt] - key) < p.window;
-          const float v = ok ? s[nt][g][i] * p.scale_log2 : kNegInf;
-          s[nt][g][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      }
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[nt], mx);
-      const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m[nt] - m_use);
-      m[nt] = m_new;
-      float ps = 0.f;
-      uint32_t packed[4];
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        float e[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          e[i] = fast_exp2(s[nt][g][i] - m_use);
-          ps += e[i];
-        }
-        packed[g * 2 + 0] = pack_bf16x2(e[0], e[1]);
-        packed[g * 2 + 1] = pack_bf16x2(e[2], e[3]);
-      }
-      lsum[nt] = lsum[nt] * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[nt][dt] *= alpha;
-      pb[nt] = as_bf16x8(u32x4{packed[0], packed[1], packed[2], packed[3]});
+      for (int dt = 0; dt < 4; ++dt) o[nt][dt] = f32x4{0, 0, 0, 0};
     }
 
-    // O^T += V^T P^T. A operand (V^T): lane = d (dt*16 + col_lo), k slots 0..3 = group A
-    // keys 4*grp..+3, slots 4..7 = group B keys 4*grp..+3 (matches the P layout above).
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    for (int seg_lo = chunk_lo; seg_lo < chunk_hi; seg_lo += kSegKeys) {
+      const int seg_hi = min(seg_lo + kSegKeys, chunk_hi);
+      if (seg_lo != chunk_lo) pid = load_page_ids(seg_lo, seg_hi);
+      const int n_steps = (seg_hi - seg_lo + 31) / 32;
+        // ---- load: K straight to registers (row = key, k = head-dim slice), V rows for LDS.
+        // Loads are unconditional: a missing second group re-reads the first group's page and
+        // tail keys read slots of an allocated page; their scores are masked and their V rows
+        // zeroed before use.
+        auto issue_loads = [&](int s, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+          const int j0 = seg_lo + 32 * s;
+          const bool hasB = (j0 + 16) < seg_hi;
+          const int pa = __builtin_amdgcn_readlane(pid, 2 * s);
+          const int pb = __builtin_amdgcn_readlane(pid, 2 * s + 1);
+          const size_t rA = cache_row(p, pa, kvh, j0 & (p.page_size - 1));
+          const size_t rB = hasB ? cache_row(p, pb, kvh, (j0 + 16) & (p.page_size - 1)) : rA;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int rsel = grp * 4 + (col_lo >> 2);
-      const int csel = dt * 16 + 4 * (col_lo & 3);
-      const s16x4 lo = lds_read_tr16(vl + rsel * kVRowBytes + csel * 2);
-      const s16x4 hi = lds_read_tr16(vl + (16 + rsel) * kVRowBytes + csel * 2);
-      u32x4 av;
-      av[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-      av[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-      av[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-      av[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+          for (int ks = 0; ks < 2; ++ks) {
+            kr[ks] = *reinterpret_cast<const u32x4*>(p.k_cache + rA + (size_t)col_lo * kHeadDim + ks * 32 + grp * 8);
+            kr[2 + ks] = *reinterpret_cast<const u32x4*>(p.k_cache + rB + (size_t)col_lo * kHeadDim + ks * 32 + grp * 8);
+          }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma16(as_bf16x8(av), pb[nt], o[nt][dt]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-  }
+          for (int ii = 0; ii < 4; ++ii) {
+            const int krow = (lane >> 3) + 8 * ii;  // 0..31
+            const size_t rr = (krow < 16) ? rA : rB;
+            vr[ii] = *reinterpret_cast<const u32x4*>(p.v_cache + rr + (size_t)(krow & 15) * kHeadDim + (lane & 7) * 8);
+          }
+        };
+        auto run_step = [&](int s, const u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+        const int j0 = seg_lo + 32 * s;
+        if (j0 + 32 > seg_hi) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int krow = (lane >> 3) + 8 * ii;
+            if (j0 + krow >= seg_hi) vr[ii] = u32x4{0, 0, 0, 0};  // keys past the range: exact zeros
+          }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int krow = (lane >> 3) + 8 * ii;
+          *reinterpret_cast<u32x4*>(vl + krow * kVRowBytes + (lane & 7) * 16) = vr[ii];
+        }
 
-  // ---- combine the 4 wave states of this chunk
+        // ---- S^T tiles: 16 keys x 16 columns per (group, nt)
+        f32x4 sc[NT][2];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float lt = lsum[nt];
-    lt += shfl_xor(lt, 16);
-    lt += shfl_xor(lt, 32);
-    lsum[nt] = lt;
-    if (grp == 0) {
-      red_m[w][nt * 16 + col_lo] = m[nt];
-      red_l[w][nt * 16 + col_lo] = lt;
-    }
-  }
-  __syncthreads();  // also: every wave is done with its V staging area
-  float* obuf = reinterpret_cast<float*>(lds);  // [NT*16 columns][64 d] fp32, reuses V staging
-  float mtot[NT], ltot[NT];
+        for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int col = nt * 16 + col_lo;
-    float M = kNegInf;
+          for (int g = 0; g < 2; ++g) {
+            f32x4 a = f32x4{0, 0, 0, 0};
+            a = mfma16(as_bf16x8(kr[2 * g]), as_bf16x8(qb[nt][0]), a);
+            a = mfma16(as_bf16x8(kr[2 * g + 1]), as_bf16x8(qb[nt][1]), a);
+            sc[nt][g] = a;
+          }
+        }
+
+        // ---- masks (only on steps that straddle a bound) + online softmax update.
+        // The running max m is lazy: it moves only when some score exceeds it by more than
+        // kLazyMax (log2 units), so most steps need neither a cross-lane reduction nor a rescale
+        // of O; every term of a column always uses that column's current m, so the result is
+        // the same softmax (terms are at most 2^kLazyMax before the final division).
+        const bool full_step = (j0 + 32 <= vis_hi_min) && (j0 >= vis_lo_max);
+        if (!full_step) {
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww][col]);
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    float Lt = 0.f;
+          for (int nt = 0; nt < NT; ++nt) {
+            const unsigned span = (unsigned)(vis_hi[nt] - vis_lo[nt]);
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) Lt += red_l[ww][col] * fast_exp2(red_m[ww][col] - Mu);
-    mtot[nt] = M;
-    ltot[nt] = Lt;
-  }
-  // Waves add their rescaled O^T into the buffer one after another (fixed order, so the
-  // result is bit-reproducible).
-  float f[NT];
+            for (int g = 0; g < 2; ++g) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float Mu = (mtot[nt] == kNegInf) ? 0.f : mtot[nt];
-    f[nt] = (ltot[nt] > 0.f) ? fast_exp2(m[nt] - Mu) / ltot[nt] : 0.f;
-  }
-  for (int ww = 0; ww < kWaves; ++ww) {
-    if (w == ww) {
+              for (int i = 0; i < 4; ++i) {
+                const int key = j0 + g * 16 + grp * 4 + i;
+                sc[nt][g][i] = ((unsigned)(key - vis_lo[nt]) < span) ? sc[nt][g][i] : kNegInf;
+              }
+            }
+          }
+        }
+        bool bump = false;
+        float mx[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int col = nt * 16 + col_lo;
+        for (int nt = 0; nt < NT; ++nt) {
+          float v = fmaxf(fmaxf(sc[nt][0][0], sc[nt][0][1]), fmaxf(sc[nt][0][2], sc[nt][0][3]));
+          v = fmaxf(v, fmaxf(fmaxf(sc[nt][1][0], sc[nt][1][1]), fmaxf(sc[nt][1][2], sc[nt][1][3])));
+          mx[nt] = v * p.scale_log2;
+          bump = bump || (mx[nt] > m[nt] + kLazyMax);
+        }
+        if (__any(bump)) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            float v = mx[nt];
+            v = fmaxf(v, shfl_xor(v, 16));
+            v = fmaxf(v, shfl_xor(v, 32));
+            const float m_new = fmaxf(m[nt], v);
+            const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m[nt] - m_new);
+            m[nt] = m_new;
+            lsum[nt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[nt][dt] *= alpha;
+          }
+        }
+        bf16x8 pbf[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float neg_m = (m[nt] == kNegInf) ? 0.0f : -m[nt];
+          float ps = 0.f;
+          uint32_t packed[4];
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            float e[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              e[i] = fast_exp2(__builtin_fmaf(sc[nt][g][i], p.scale_log2, neg_m));
+              ps += e[i];
+            }
+            packed[g * 2 + 0] = pack_bf16x2(e[0], e[1]);
+            packed[g * 2 + 1] = pack_bf16x2(e[2], e[3]);
+          }
+          lsum[nt] += ps;
+          pbf[nt] = as_bf16x8(u32x4{packed[0], packed[1], packed[2], packed[3]});
+        }
+
+        // ---- O^T += V^T P^T. A operand (V^T): lane = d (dt*16 + col_lo), k slots 0..3 =
+        // group A keys 4*grp..+3, slots 4..7 = group B keys 4*grp..+3 (the P layout above).
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          f32x4* dst = reinterpret_cast<f32x4*>(&obuf[col * kHeadDim + dt * 16 + grp * 4]);
-          const f32x4 add = o[nt][dt] * f[nt];
-          *dst = (ww == 0) ? add : (*dst + add);
+          const int rsel = grp * 4 + (col_lo >> 2);
+          const int csel = dt * 16 + 4 * (col_lo & 3);
+          const s16x4 lo = lds_read_tr16(vl + rsel * kVRowBytes + csel * 2);
+          const s16x4 hi = lds_read_tr16(vl + (16 + rsel) * kVRowBytes + csel * 2);
+          const u32x4 av = join_tr16(lo, hi);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma16(as_bf16x8(av), pbf[nt], o[nt][dt]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        };
+
+        // Two steps in flight per wave (ping-pong register buffers); this wave owns steps
+        // w, w + 4, w + 8, ... of the segment.
+        // This wave owns steps w, w + 4, w + 8, ... of the segment.
+        const int n_mine = (w < n_steps) ? (n_steps - w + kWaves - 1) / kWaves : 0;
+        for (int k = 0; k < n_mine; ++k) {
+          u32x4 kA[4], vA[4];
+          issue_loads(w + kWaves * k, kA, vA);
+          run_step(w + kWaves * k, kA, vA);
+        }
+    }
+
+    // ---- plan: chunk counts and partial offsets (one writer per sequence)
+    if (c == 0 && kvh == 0 && w == 0) {
+      if (lane < p.q_len) {
+        p.counts[b * p.q_len + lane] = n_b;
+        p.indptr[b * p.q_len + lane] = base + lane * n_b;
+      }
+      if (b == p.batch - 1 && lane == 0) p.indptr[p.batch * p.q_len] = base + p.q_len * n_b;
+    }
+
+    // ---- combine the 4 wave states of this chunk
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float lt = lsum[nt];
+      lt += shfl_xor(lt, 16);
+      lt += shfl_xor(lt, 32);
+      if (grp == 0) {
+        red_m[w][nt * 16 + col_lo] = m[nt];
+        red_l[w][nt * 16 + col_lo] = lt;
+      }
+    }
+    __syncthreads();  // also: every wave is done with its V staging area
+    float* obuf = reinterpret_cast<float*>(lds);  // [NT*16 columns][64 d] fp32, reuses V staging
+    float mtot[NT], ltot[NT], f[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = nt * 16 + col_lo;
+      float M = kNegInf;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww][col]);
+      const float Mu = (M == kNegInf) ? 0.f : M;
+      float Lt = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) Lt += red_l[ww][col] * fast_exp2(red_m[ww][col] - Mu);
+      mtot[nt] = M;
+      ltot[nt] = Lt;
+      f[nt] = (Lt > 0.f) ? fast_exp2(m[nt] - Mu) / Lt : 0.f;
+    }
+    // Waves add their rescaled O^T into the buffer one after another (fixed order, so the
+    // result is bit-reproducible).
+    for (int ww = 0; ww < kWaves; ++ww) {
+      if (w == ww) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int col = nt * 16 + col_lo;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            f32x4* dst = reinterpret_cast<f32x4*>(&obuf[col * kHeadDim + dt * 16 + grp * 4]);
+            const f32x4 add = o[nt][dt] * f[nt];
+            *dst = (ww == 0) ? add : (*dst + add);
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- write the partial: o_c (normalised), lse_c (natural log)
+    for (int i = threadIdx.x; i < R * (kHeadDim / 4); i += kThreads) {
+      const int col = i / (kHeadDim / 4);
+      const int d4 = (i % (kHeadDim / 4)) * 4;
+      const int t = col / G, gh = col % G;
+      const int pidx = base + t * n_b + c;
+      const int h = kvh * G + gh;
+      const f32x4 val = *reinterpret_cast<const f32x4*>(&obuf[col * kHeadDim + d4]);
+      *reinterpret_cast<f32x4*>(p.o_part + ((size_t)pidx * p.hq + h) * kHeadDim + d4) = val;
+    }
+    if (w == 0 && lane < 16) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = nt * 16 + lane;
+        if (col < R) {
+          const int t = col / G, gh = col % G;
+          const int pidx = base + t * n_b + c;
+          const float M = mtot[nt], Lt = ltot[nt];
+          const float lse = (M == kNegInf || !(Lt > 0.f)) ? kNegInf : (M + fast_log2(Lt)) * kLn2;
+          p.lse_part[(size_t)pidx * p.hq + kvh * G + gh] = lse;
         }
       }
     }
-    __syncthreads();
-  }
-
-  // ---- write the partial: o_c (normalised), lse_c (natural log)
-  for (int i = threadIdx.x; i < R * (kHeadDim / 4); i += kThreads) {
-    const int col = i / (kHeadDim / 4);
-    const int d4 = (i % (kHeadDim / 4)) * 4;
-    const int t = col / G, gh = col % G;
-    const int pidx = base + t * n_b + c;
-    const int h = kvh * G + gh;
-    f32x4 val = *reinterpret_cast<const f32x4*>(&obuf[col * kHeadDim + d4]);
-    *reinterpret_cast<f32x4*>(p.o_part + ((size_t)pidx * p.hq + h) * kHeadDim + d4) = val;
-  }
-  if (w == 0 && lane < 16) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int col = nt * 16 + lane;
-      if (col < R) {
-        const int t = col / G, gh = col % G;
-        const int pidx = base + t * n_b + c;
-        const float M = mtot[nt], Lt = ltot[nt];
-        const float lse = (M == kNegInf || !(Lt > 0.f)) ? kNegInf : (M + fast_log2(Lt)) * kLn2;
-        p.lse_part[(size_t)pidx * p.hq + kvh * G + gh] = lse;
-      }
-    }
+    __syncthreads();  // obuf (V staging) and red_* are reused by the next item
   }
 }
+
+namespace {
+template <int NT>
+int resident_blocks_per_cu() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<NT>, kThreads, 0) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+
+struct DeviceShape {
+  int cus = 0;
+  int blocks_per_cu[5] = {0, 0, 0, 0, 0};
+};
+
+// Per-device launch shape, computed once per device from host-side queries.
+const DeviceShape& device_shape() {
+  static DeviceShape shapes[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  DeviceShape& s = shapes[dev];
+  if (s.cus == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    s.blocks_per_cu[1] = resident_blocks_per_cu<1>();
+    s.blocks_per_cu[2] = resident_blocks_per_cu<2>();
+    s.blocks_per_cu[3] = resident_blocks_per_cu<3>();
+    s.blocks_per_cu[4] = resident_blocks_per_cu<4>();
+    s.cus = cus;
+  }
+  return s;
+}
+}  // namespace
 
 hipError_t launch_decode_split(const DecodeParams& p, int max_chunks, hipStream_t stream) {
   const int R = p.q_len * p.group;
   const int nt = (R + 15) / 16;
-  dim3 grid(max_chunks * p.batch, p.hkv), block(kThreads);
+  if (nt < 1 || nt > 4) return hipErrorInvalidValue;
+  const DeviceShape& ds = device_shape();
+  // Persistent grid: enough workgroups to fill every CU, never more than the item bound.
+  const long item_bound = (long)max_chunks * p.batch * p.hkv;
+  long blocks = (long)ds.cus * ds.blocks_per_cu[nt];
+  if (blocks > item_bound) blocks = item_bound;
+  if (blocks < 1) blocks = 1;
+  dim3 grid((unsigned)blocks), block(kThreads);
   switch (nt) {
     case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, block, 0, stream, p); break;
     case 3: hipLaunchKernelGGL(decode_split_kernel<3>, grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(decode_split_kernel<4>, grid, block, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
+    default: hipLaunchKernelGGL(decode_split_kernel<4>, grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }

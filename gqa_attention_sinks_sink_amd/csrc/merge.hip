@@ -2,42 +2,78 @@
 // sinks": attention split into blocks along the sequence length; each block's partial
 // is its normalised output and log-sum-exp, the sink counted in the first block only).
 //
-// One wave per (row, head); lane = head-dim element. Partial weights are
-// exp(lse_c - max lse); partials at -inf weigh 0.
+// 16 threads per (row, head), 4 head-dim elements (16 B) per thread. Partials are read
+// 8 at a time with independent loads and folded into a running (max, weight sum, sum)
+// triple, so a row of n partials costs ceil(n / 8) memory round trips. Partials at -inf
+// weigh 0; a row with no live partial yields out = 0, lse = -inf.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace attn_sink {
 
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  const int lane = threadIdx.x & 63;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int r = blockIdx.x;
-  if (h >= p.hq) return;
+namespace {
+constexpr int kThreads = 256;
+constexpr int kPairsPerBlock = kThreads / 16;
+constexpr int kBatch = 8;
+}  // namespace
+
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
+  const long pair = (long)blockIdx.x * kPairsPerBlock + (threadIdx.x >> 4);
+  if (pair >= (long)p.rows * p.hq) return;
+  const int r = (int)(pair / p.hq);
+  const int h = (int)(pair - (long)r * p.hq);
+  const int d4 = (threadIdx.x & 15) * 4;
   const int p0 = clampi(p.indptr[r], 0, p.num_partials);
   const int p1 = clampi(p.indptr[r + 1], p0, p.num_partials);
 
-  float M = kNegInf;
-  for (int i = p0; i < p1; ++i) M = fmaxf(M, p.lse_part[(size_t)i * p.hq + h]);
-  float acc = 0.f, W = 0.f;
-  if (M != kNegInf) {
-    for (int i = p0; i < p1; ++i) {
-      const float wgt = fast_exp2((p.lse_part[(size_t)i * p.hq + h] - M) * kLog2e);
-      W += wgt;
-      acc += wgt * p.o_part[((size_t)i * p.hq + h) * kHeadDim + lane];
+  float M = kNegInf, W = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = p0; i0 < p1; i0 += kBatch) {
+    float l[kBatch];
+    f32x4 o[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u;
+      if (i < p1) {
+        l[u] = p.lse_part[(size_t)i * p.hq + h] * kLog2e;
+        o[u] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)i * p.hq + h) * kHeadDim + d4);
+      } else {
+        l[u] = kNegInf;
+        o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+    float bm = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) bm = fmaxf(bm, l[u]);
+    const float Mn = fmaxf(M, bm);
+    if (Mn == kNegInf) continue;
+    const float s = fast_exp2(M - Mn);  // 0 when M is still -inf
+    W *= s;
+    acc *= s;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float wu = fast_exp2(l[u] - Mn);
+      W += wu;
+      acc += o[u] * wu;
+    }
+    M = Mn;
   }
-  const float o = (W > 0.f) ? acc / W : 0.f;
-  p.out[((size_t)r * p.hq + h) * kHeadDim + lane] = (uint16_t)f32_to_bf16_bits(o);
-  if (p.lse != nullptr && lane == 0) {
-    p.lse[(size_t)r * p.hq + h] = (W > 0.f) ? M + fast_log2(W) * kLn2 : kNegInf;
+  const float inv = (W > 0.f) ? 1.0f / W : 0.f;
+  u32x2 pk;
+  pk[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2*>(p.out + ((size_t)r * p.hq + h) * kHeadDim + d4) = pk;
+  if (p.lse != nullptr && d4 == 0) {
+    p.lse[(size_t)r * p.hq + h] = (W > 0.f) ? (M + fast_log2(W)) * kLn2 : kNegInf;
   }
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
-  if (p.rows == 0 || p.hq == 0) return hipSuccess;
-  dim3 grid(p.rows, (p.hq + 3) / 4), block(256);
-  hipLaunchKernelGGL(merge_kernel, grid, block, 0, stream, p);
+  const long pairs = (long)p.rows * p.hq;
+  if (pairs == 0) return hipSuccess;
+  const long blocks = (pairs + kPairsPerBlock - 1) / kPairsPerBlock;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -25,13 +25,15 @@ constexpr int kThreads = 256;
 constexpr int kTileN = 64;        // keys per tile
 constexpr int kKRowBytes = 144;   // K tile row stride (128 B + 16): conflict-free 16 B reads
 constexpr int kVRowBytes = 192;   // V tile row stride (128 B + 64): conflict-free transposing reads
+constexpr float kLazyMax = 8.0f;  // running-max slack (log2 units) before a rescale
 }  // namespace
 
 template <int GP>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   constexpr int TOK = 128 / GP;
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[kTileN * kKRowBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[kTileN * kVRowBytes];
+  // Double-buffered K/V tiles: the next tile is written while the current one is read.
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kTileN * kKRowBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][kTileN * kVRowBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -80,38 +82,62 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) { o[0][i] = 0.f; o[1][i] = 0.f; }
 
-  // Key range of the workgroup and per-wave position range (for mask decisions).
+  // Key range of the workgroup; keys visible to this lane's row: [vis_lo, vis_hi).
   const int p_lo = off + ts, p_hi = off + te - 1;
   int jb = (p.window > 0) ? max(0, p_lo - p.window + 1) : 0;
   jb &= ~(kTileN - 1);
-  int je = p.causal ? min(Lk, p_hi + 1) : Lk;
-  const int wt0 = min(ts + (w * 32) / GP, te - 1), wt1 = min(ts + (w * 32 + 31) / GP, te - 1);
-  const int wp_min = off + wt0, wp_max = off + wt1;
+  const int je = p.causal ? min(Lk, p_hi + 1) : Lk;
+  int vis_hi = p.causal ? min(Lk, pos + 1) : Lk;
+  const int vis_lo = (p.window > 0) ? max(0, pos - p.window + 1) : 0;
+  if (vis_hi < vis_lo) vis_hi = vis_lo;
+  const unsigned vis_span = (unsigned)(vis_hi - vis_lo);
+  // Wave-wide bounds over the wave's valid rows: a tile inside [lo_max, hi_min) needs no mask.
+  int hi_min = row_ok ? vis_hi : 0x7fffffff, lo_max = row_ok ? vis_lo : -0x7fffffff;
+#pragma unroll
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+    hi_min = min(hi_min, __shfl_xor(hi_min, o2, 64));
+    lo_max = max(lo_max, __shfl_xor(lo_max, o2, 64));
+  }
 
-  for (int jt = jb; jt < je; jt += kTileN) {
-    // Stage K and V rows jt..jt+63 (16 B per thread per row chunk); rows past Lk are zero.
-    u32x4 kr[2], vr[2];
+  // K/V staging: thread covers rows (tid >> 3) and (tid >> 3) + 32, 16 B chunk (tid & 7).
+  auto load_tile = [&](int jt, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-      const int row = (tid >> 3) + 32 * ii;
-      const int j = jt + row;
+      const int j = jt + (tid >> 3) + 32 * ii;
       if (j < Lk) {
         const size_t g = ((size_t)(k0 + j) * p.hkv + kvh) * kHeadDim + (tid & 7) * 8;
         kr[ii] = *reinterpret_cast<const u32x4*>(p.k + g);
         vr[ii] = *reinterpret_cast<const u32x4*>(p.v + g);
       } else {
-        kr[ii] = u32x4{0, 0, 0, 0};
+        kr[ii] = u32x4{0, 0, 0, 0};  // keys past the sequence: exact zeros
         vr[ii] = u32x4{0, 0, 0, 0};
       }
     }
-    __syncthreads();  // previous tile fully consumed
+  };
+  auto store_tile = [&](int buf, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int row = (tid >> 3) + 32 * ii;
-      *reinterpret_cast<u32x4*>(k_lds + row * kKRowBytes + (tid & 7) * 16) = kr[ii];
-      *reinterpret_cast<u32x4*>(v_lds + row * kVRowBytes + (tid & 7) * 16) = vr[ii];
+      *reinterpret_cast<u32x4*>(k_lds[buf] + row * kKRowBytes + (tid & 7) * 16) = kr[ii];
+      *reinterpret_cast<u32x4*>(v_lds[buf] + row * kVRowBytes + (tid & 7) * 16) = vr[ii];
     }
-    __syncthreads();
+  };
+
+  if (jb < je) {
+    u32x4 kr[2], vr[2];
+    load_tile(jb, kr, vr);
+    store_tile(0, kr, vr);
+  }
+  __syncthreads();
+
+  int buf = 0;
+  for (int jt = jb; jt < je; jt += kTileN, buf ^= 1) {
+    // Next tile's K/V go to registers now and to the other LDS buffer after this tile's math.
+    const bool has_next = jt + kTileN < je;
+    u32x4 kn[2], vn[2];
+    if (has_next) load_tile(jt + kTileN, kn, vn);
+    const unsigned char* kt_lds = k_lds[buf];
+    const unsigned char* vt_lds = v_lds[buf];
 
     // S^T: 2 x (32 keys x 32 rows), k = 64 in 4 steps.
     f32x16 s[2];
@@ -121,55 +147,54 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(k_lds + (kt * 32 + r32) * kKRowBytes + (ks * 16 + half * 8) * 2);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kt_lds + (kt * 32 + r32) * kKRowBytes + (ks * 16 + half * 8) * 2);
         s[kt] = mfma32(as_bf16x8(a), as_bf16x8(qb[ks]), s[kt]);
       }
     }
 
-    // Masks (only on tiles that straddle a boundary for this wave).
-    const bool need_mask = (jt + kTileN > Lk) || (p.causal && jt + kTileN - 1 > wp_min) ||
-                           (p.window > 0 && wp_max - jt >= p.window);
-    if (need_mask) {
+    // Masks only on tiles that straddle a row's visible range.
+    if (!(jt >= lo_max && jt + kTileN <= hi_min)) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int j = jt + kt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          bool ok = j < Lk;
-          if (p.causal) ok = ok && j <= pos;
-          if (p.window > 0) ok = ok && (pos - j) < p.window;
-          s[kt][i] = ok ? s[kt][i] : kNegInf;
+          s[kt][i] = ((unsigned)(j - vis_lo) < vis_span) ? s[kt][i] : kNegInf;
         }
       }
     }
 
+    // Lazy running max (log2 units): it moves only when a score exceeds it by more than
+    // kLazyMax, so most tiles need neither the cross-lane max nor a rescale of O. Every term
+    // of a row uses the row's current m, so the softmax is unchanged.
     float mx = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
     }
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx * p.scale_log2);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
+    mx *= p.scale_log2;
+    if (__any(mx > m + kLazyMax)) {
+      const float m_new = fmaxf(m, fmaxf(mx, shfl_xor(mx, 32)));
+      const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { o[0][i] *= alpha; o[1][i] *= alpha; }
+    }
+    const float neg_m = (m == kNegInf) ? 0.f : -m;
 
     float ps = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(__builtin_fmaf(s[kt][i], p.scale_log2, -m_use));
+        const float e = fast_exp2(__builtin_fmaf(s[kt][i], p.scale_log2, neg_m));
         s[kt][i] = e;
         ps += e;
       }
     }
-    lsum = lsum * alpha + ps;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { o[0][i] *= alpha; o[1][i] *= alpha; }
-    }
+    lsum += ps;
 
     // O^T += V^T P^T over 4 steps of 16 keys.
 #pragma unroll
@@ -186,16 +211,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         const int c0 = dt * 32 + 16 * (grp & 1) + 4 * (jl & 3);
-        const s16x4 lo = lds_read_tr16(v_lds + krow * kVRowBytes + c0 * 2);
-        const s16x4 hi = lds_read_tr16(v_lds + (krow + 8) * kVRowBytes + c0 * 2);
-        u32x4 av;
-        av[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-        av[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-        av[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-        av[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+        const s16x4 lo = lds_read_tr16(vt_lds + krow * kVRowBytes + c0 * 2);
+        const s16x4 hi = lds_read_tr16(vt_lds + (krow + 8) * kVRowBytes + c0 * 2);
+        const u32x4 av = join_tr16(lo, hi);
         o[dt] = mfma32(as_bf16x8(av), as_bf16x8(pw), o[dt]);
       }
     }
+
+    if (has_next) store_tile(buf ^ 1, kn, vn);
+    __syncthreads();
   }
 
   // Epilogue: out = O / d, lse = m + log2(d) converted to natural log.
