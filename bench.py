@@ -79,13 +79,28 @@ def measured_traffic(name, kind):
 
 
 def time_calls(torch, fn, steps, warmup):
+    """Average ms per step over exactly `steps` steps after `warmup` eager steps.
+
+    The steps are captured once into a HIP graph and replayed, so host launch overhead does not
+    enter the device timing; HIP events bracket the replay on the stream the kernels run on.
+    """
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            fn()
+    torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    for _ in range(steps):
-        fn()
+    graph.replay()
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / steps

@@ -330,3 +330,53 @@ def test_decode_full_size(amd, name):
     seqs = list(range(spec.batch)) if name == "paged_decode" else [0, 1, 7, 19, 31]
     ro, rl = oracle_decode(inp, spec, seqs=seqs)
     assert_close(out, lse, ro, rl, name)
+
+
+# -------------------------------------------------------------------------------------------
+# graph capture: launches depend on host scalars only, so calls can be captured and replayed
+# -------------------------------------------------------------------------------------------
+def test_graph_capture_replays_match_eager(amd):
+    spec = scaled(CONFIGS["verify"], batch=4, kv_len=(100, 1500), hq=16, hkv=2, seed=69)
+    inp = make_paged(spec)
+    d = dev_paged(inp)
+    need = amd.attn_sink_decode_workspace_size(4, spec.q_len, inp["max_kv_len"], spec.hq, 64, spec.kv_chunk)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(d["q"].shape[0], spec.hq, device=DEV)
+    pspec = scaled(CONFIGS["causal_prefill"], batch=2, hq=8, hkv=2, seed=70)
+    pin = make_varlen(pspec, seqlens=[200, 77])
+    pq, pk, pv = tbits(pin["q"]), tbits(pin["k"]), tbits(pin["v"])
+    cu = torch.from_numpy(pin["cu_seqlens"]).to(DEV)
+    ps = torch.from_numpy(pin["sinks"]).to(DEV)
+    pout = torch.empty_like(pq)
+    plse = torch.empty(pq.shape[0], pspec.hq, device=DEV)
+
+    def step():
+        amd.attn_sink_decode_paged(d["q"], d["k"], d["v"], d["table"], d["lens"], d["sinks"], spec.q_len,
+                                   inp["max_kv_len"], spec.scale, True, 0, spec.kv_chunk, workspace=ws, out=out,
+                                   lse=lse)
+        amd.attn_sink_prefill(pq, pk, pv, ps, cu, cu, 200, 200, pspec.scale, True, 0, out=pout, lse=plse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, lse, pout, plse)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    scratch = torch.randn(512, 512, device=DEV)
+    for rep in range(3):
+        for t in (out, lse, pout, plse):
+            t.zero_()
+        scratch = scratch @ scratch.T / 512.0          # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((out, lse, pout, plse), ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), f"replay {rep}"
