@@ -71,6 +71,25 @@ __device__ __forceinline__ u32x4 join_tr16(s16x4 lo, s16x4 hi) {
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// Raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes return zero
+// without touching memory (CDNA buffer range check), so tails need no branches. The range
+// check covers the VGPR offset; the SGPR offset is kept at zero so every byte is checked.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// 16 bytes per lane from a buffer straight into LDS (no VGPRs): lane i of the wave writes
+// lds_base + 16 * i, where lds_base is wave-uniform.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (n < 16), leaving the other counters alone.
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
+
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }

@@ -44,10 +44,15 @@ struct PrefillParams {
   int batch, total_q, total_kv, max_q, max_kv;
   int hq, hkv, group, causal, window;
   float scale_log2;
+  int units;        // work units per (sequence, head group); set by the launcher
+  int pair_blocks;  // causal pairing of row blocks u and n-1-u; set by the launcher
 };
 
 hipError_t launch_decode_split(const DecodeParams& p, int max_chunks, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+// Prefill launch shape: query heads packed per tile row block, and 32-row blocks per wave.
+int prefill_heads_per_tile(int group);
+int prefill_row_blocks(int max_q, int heads_per_tile);
 
 }  // namespace attn_sink
