@@ -47,8 +47,13 @@ def parse():
                     choices=["paged_decode", "verify", "causal_prefill", "window_prefill", "embed", "tiny_causal"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU oracle sample (wall seconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timing (profiling runs: every call is then a warm, timed one)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs (workload, then the plain copy) into "
+                         "profiles/traffic.json for --workload; runs on the host only")
     return ap.parse_args()
 
 
@@ -76,6 +81,58 @@ def measured_traffic(name, kind):
     if rec is None or rec.get("source_hash") != source_hash(kind):
         return None
     return rec.get("bytes_per_launch")
+
+
+def _pmc_per_dispatch(directory, counter):
+    """{dispatch id: (kernel name, value)} for one counter of a rocprofv3 --pmc CSV output."""
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                key = row["Dispatch_Id"]
+                name, v = vals.get(key, (row["Kernel_Name"], 0.0))
+                vals[key] = (name, v + float(row["Counter_Value"]))
+    return vals
+
+
+def record_traffic(name, kind, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB
+    per dispatch), each scaled so that a plain 1 GiB device copy reads and writes 1 GiB."""
+    kernel = "decode_split_kernel" if kind == "decode" else "prefill_kernel"
+
+    def mean_for(directory, counter, pattern):
+        v = [val for (k, val) in _pmc_per_dispatch(directory, counter).values() if pattern in k]
+        if not v:
+            raise SystemExit(f"no {counter} dispatch of {pattern} under {directory}")
+        return float(np.mean(v)), len(v)
+
+    def copy_kib(directory, counter):
+        v = [val for (_, val) in _pmc_per_dispatch(directory, counter).values()]
+        return max(v)
+
+    gib_kib = float(1 << 20)
+    f_scale = gib_kib / copy_kib(copy_fetch_dir, "FETCH_SIZE")
+    w_scale = gib_kib / copy_kib(copy_write_dir, "WRITE_SIZE")
+    fetch_kib, nf = mean_for(fetch_dir, "FETCH_SIZE", kernel)
+    write_kib, nw = mean_for(write_dir, "WRITE_SIZE", kernel)
+    fetch_b = fetch_kib * 1024 * f_scale
+    write_b = write_kib * 1024 * w_scale
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            data = json.load(fh)
+    data[name] = {"kernel": kernel, "source_hash": source_hash(kind), "bytes_per_launch": int(fetch_b + write_b),
+                  "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+                  "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                  "dispatches": {"fetch": nf, "write": nw}}
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print(json.dumps({name: data[name]}))
 
 
 def time_calls(torch, fn, steps, warmup):
@@ -107,10 +164,15 @@ def time_calls(torch, fn, steps, warmup):
 
 
 def cold_time(torch, fn, steps, scratch):
-    """Median per-call time with a 1 GiB write before each call (L2 and MALL flushed)."""
+    """Median per-call time with a 1 GiB read before each call (L2 and MALL flushed).
+
+    The flush reads a buffer written once beforehand: a write-based flush would leave dirty
+    lines whose write-back competes with the timed call."""
     ts = []
+    scratch.fill_(1)
+    flat = scratch.view(torch.int64)
     for _ in range(steps):
-        scratch.fill_(1)
+        flat.sum()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         fn()
@@ -219,9 +281,11 @@ def bench_paged(args, torch, amd, name):
     merge_ms = time_calls(torch, lambda: amd.attn_sink_merge_partials(o_p, l_p, indptr, out=out2, return_lse=False),
                           args.steps, args.warmup)
     split_ms = max(ms - merge_ms, 1e-6)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cold_ms = cold_time(torch, step, max(5, min(args.steps, 20)), scratch)
-    del scratch
+    cold_ms = None
+    if not args.no_cold:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold_ms = cold_time(torch, step, max(5, min(args.steps, 20)), scratch)
+        del scratch
 
     value = algo_bytes / (ms * 1e-3) / 1e9
     achieved = kernel_bytes / (split_ms * 1e-3) / 1e9
@@ -238,9 +302,10 @@ def bench_paged(args, torch, amd, name):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(name, "decode"), "algorithmic_bytes_per_launch": kernel_bytes,
                      "kernel_ms": round(split_ms, 5), "merge_ms": round(merge_ms, 5)},
-        "cold_l2_mall_ms_per_step": round(cold_ms, 5),
-        "cold_value": round(algo_bytes / (cold_ms * 1e-3) / 1e9, 1),
     }
+    if cold_ms is not None:
+        res["cold_l2_mall_ms_per_step"] = round(cold_ms, 5)
+        res["cold_value"] = round(algo_bytes / (cold_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
         v, n, dt = cpu_baseline_paged(inp, spec, args.cpu_seconds, kv_bytes_seq)
         res["cpu_baseline"] = {"value": round(v, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -320,6 +385,10 @@ def bench_varlen(args, torch, amd, name):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        kind = "decode" if args.workload in ("paged_decode", "verify") else "prefill"
+        record_traffic(args.workload, kind, *args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this build measures the "
               f"one-GPU shard of the path).", file=sys.stderr)

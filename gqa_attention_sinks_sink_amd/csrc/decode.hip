@@ -73,19 +73,26 @@ __device__ __forceinline__ size_t cache_row(const DecodeParams& p, int page, int
 
 }  // namespace
 
-// Minimum resident waves per SIMD requested per column-tile count. The kernel is bound by
-// memory latency, so register pressure is traded for waves in flight (measured on MI355X).
+// Resident waves per SIMD and steps of loads in flight per wave, per column-tile count
+// (measured on MI355X). With one tile (single-token decode) the step math is short and 4
+// waves per SIMD with one step each stream best; with more tiles the step math is longer,
+// so each wave keeps two steps in flight and the register budget sets the occupancy.
 template <int NT>
 struct DecodeOccupancy { static constexpr int value = 1; };
 template <> struct DecodeOccupancy<1> { static constexpr int value = 4; };
-template <> struct DecodeOccupancy<2> { static constexpr int value = 3; };
-template <> struct DecodeOccupancy<3> { static constexpr int value = 4; };
-template <> struct DecodeOccupancy<4> { static constexpr int value = 2; };
+template <> struct DecodeOccupancy<2> { static constexpr int value = 2; };
+template <> struct DecodeOccupancy<3> { static constexpr int value = 2; };
+template <> struct DecodeOccupancy<4> { static constexpr int value = 1; };
+template <int NT>
+constexpr int kStepsInFlight = (NT == 1) ? 1 : 2;
 
 template <int NT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DecodeOccupancy<NT>::value, 8)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(DecodeOccupancy<NT>::value, DecodeOccupancy<NT>::value)))
 void decode_split_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * kVWaveBytes];
+  // Per-wave LDS region: V staging of a step, then the wave's O^T for the combine.
+  constexpr int kWaveRegion = (kVWaveBytes > NT * 16 * kHeadDim * 4) ? kVWaveBytes : NT * 16 * kHeadDim * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * kWaveRegion];
   __shared__ float red_m[kWaves][NT * 16];
   __shared__ float red_l[kWaves][NT * 16];
 
@@ -95,7 +102,7 @@ void decode_split_kernel(DecodeParams p) {
   const int R = p.q_len * G;  // live columns
   const int col_lo = lane & 15;
   const int grp = lane >> 4;  // 16-lane group 0..3
-  unsigned char* vl = lds + w * kVWaveBytes;
+  unsigned char* vl = lds + w * kWaveRegion;
 
   // ---- total number of (sequence, chunk) pairs, and a cursor over sequences
   int tot = 0;
@@ -338,14 +345,35 @@ void decode_split_kernel(DecodeParams p) {
         __builtin_amdgcn_wave_barrier();
         };
 
-        // Two steps in flight per wave (ping-pong register buffers); this wave owns steps
-        // w, w + 4, w + 8, ... of the segment.
-        // This wave owns steps w, w + 4, w + 8, ... of the segment.
+        // This wave owns steps w, w + 4, w + 8, ... of the segment, with two steps in
+        // flight (ping-pong register buffers): the loads of step k + 1 are issued before
+        // step k is computed.
         const int n_mine = (w < n_steps) ? (n_steps - w + kWaves - 1) / kWaves : 0;
-        for (int k = 0; k < n_mine; ++k) {
-          u32x4 kA[4], vA[4];
-          issue_loads(w + kWaves * k, kA, vA);
-          run_step(w + kWaves * k, kA, vA);
+        if constexpr (kStepsInFlight<NT> == 1) {
+          for (int k = 0; k < n_mine; ++k) {
+            u32x4 kA[4], vA[4];
+            issue_loads(w + kWaves * k, kA, vA);
+            run_step(w + kWaves * k, kA, vA);
+          }
+        } else {
+          // The steady-state loop issues its loads unconditionally, so the compiler waits for
+          // exactly the older step's loads (a conditional load makes it wait for all of them).
+          u32x4 kA[4], vA[4], kB[4], vB[4];
+          int k = 0;
+          if (n_mine > 0) issue_loads(w, kA, vA);
+          for (; k + 2 < n_mine; k += 2) {
+            issue_loads(w + kWaves * (k + 1), kB, vB);
+            run_step(w + kWaves * k, kA, vA);
+            issue_loads(w + kWaves * (k + 2), kA, vA);
+            run_step(w + kWaves * (k + 1), kB, vB);
+          }
+          if (k + 1 < n_mine) {
+            issue_loads(w + kWaves * (k + 1), kB, vB);
+            run_step(w + kWaves * k, kA, vA);
+            run_step(w + kWaves * (k + 1), kB, vB);
+          } else if (k < n_mine) {
+            run_step(w + kWaves * k, kA, vA);
+          }
         }
     }
 
@@ -358,7 +386,10 @@ void decode_split_kernel(DecodeParams p) {
       if (b == p.batch - 1 && lane == 0) p.indptr[p.batch * p.q_len] = base + p.q_len * n_b;
     }
 
-    // ---- combine the 4 wave states of this chunk
+    // ---- combine the 4 wave states of this chunk. Each wave leaves its (m, d) per column and
+    // its unnormalised O^T in its own LDS region (which held its V staging); after one
+    // barrier every thread merges 4 columns x 4 head-dim values over the waves in a fixed
+    // order (bit-reproducible) and writes the chunk partial: o_c = O / d, lse_c = m + ln d.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float lt = lsum[nt];
@@ -368,66 +399,36 @@ void decode_split_kernel(DecodeParams p) {
         red_m[w][nt * 16 + col_lo] = m[nt];
         red_l[w][nt * 16 + col_lo] = lt;
       }
-    }
-    __syncthreads();  // also: every wave is done with its V staging area
-    float* obuf = reinterpret_cast<float*>(lds);  // [NT*16 columns][64 d] fp32, reuses V staging
-    float mtot[NT], ltot[NT], f[NT];
+      float* slot = reinterpret_cast<float*>(vl);  // [NT*16 columns][64 d]
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int col = nt * 16 + col_lo;
+      for (int dt = 0; dt < 4; ++dt)
+        *reinterpret_cast<f32x4*>(&slot[(nt * 16 + col_lo) * kHeadDim + dt * 16 + grp * 4]) = o[nt][dt];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < R * (kHeadDim / 4); i += kThreads) {
+      const int col = i / (kHeadDim / 4);
+      const int d4 = (i % (kHeadDim / 4)) * 4;
       float M = kNegInf;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww][col]);
       const float Mu = (M == kNegInf) ? 0.f : M;
       float Lt = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) Lt += red_l[ww][col] * fast_exp2(red_m[ww][col] - Mu);
-      mtot[nt] = M;
-      ltot[nt] = Lt;
-      f[nt] = (Lt > 0.f) ? fast_exp2(m[nt] - Mu) / Lt : 0.f;
-    }
-    // Waves add their rescaled O^T into the buffer one after another (fixed order, so the
-    // result is bit-reproducible).
-    for (int ww = 0; ww < kWaves; ++ww) {
-      if (w == ww) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = nt * 16 + col_lo;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            f32x4* dst = reinterpret_cast<f32x4*>(&obuf[col * kHeadDim + dt * 16 + grp * 4]);
-            const f32x4 add = o[nt][dt] * f[nt];
-            *dst = (ww == 0) ? add : (*dst + add);
-          }
-        }
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float sc = fast_exp2(red_m[ww][col] - Mu);
+        Lt += red_l[ww][col] * sc;
+        const float* slot = reinterpret_cast<const float*>(lds + ww * kWaveRegion);
+        acc += *reinterpret_cast<const f32x4*>(&slot[col * kHeadDim + d4]) * sc;
       }
-      __syncthreads();
-    }
-
-    // ---- write the partial: o_c (normalised), lse_c (natural log)
-    for (int i = threadIdx.x; i < R * (kHeadDim / 4); i += kThreads) {
-      const int col = i / (kHeadDim / 4);
-      const int d4 = (i % (kHeadDim / 4)) * 4;
+      const float inv = (Lt > 0.f) ? 1.0f / Lt : 0.f;
       const int t = col / G, gh = col % G;
       const int pidx = base + t * n_b + c;
       const int h = kvh * G + gh;
-      const f32x4 val = *reinterpret_cast<const f32x4*>(&obuf[col * kHeadDim + d4]);
-      *reinterpret_cast<f32x4*>(p.o_part + ((size_t)pidx * p.hq + h) * kHeadDim + d4) = val;
+      *reinterpret_cast<f32x4*>(p.o_part + ((size_t)pidx * p.hq + h) * kHeadDim + d4) = acc * inv;
+      if (d4 == 0) p.lse_part[(size_t)pidx * p.hq + h] = (M == kNegInf || !(Lt > 0.f)) ? kNegInf : (M + fast_log2(Lt)) * kLn2;
     }
-    if (w == 0 && lane < 16) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int col = nt * 16 + lane;
-        if (col < R) {
-          const int t = col / G, gh = col % G;
-          const int pidx = base + t * n_b + c;
-          const float M = mtot[nt], Lt = ltot[nt];
-          const float lse = (M == kNegInf || !(Lt > 0.f)) ? kNegInf : (M + fast_log2(Lt)) * kLn2;
-          p.lse_part[(size_t)pidx * p.hq + kvh * G + gh] = lse;
-        }
-      }
-    }
-    __syncthreads();  // obuf (V staging) and red_* are reused by the next item
+    __syncthreads();  // the LDS regions and red_* are reused by the next item
   }
 }
 
