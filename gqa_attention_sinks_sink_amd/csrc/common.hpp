@@ -87,6 +87,31 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
 }
 
+// The same 16-byte buffer -> LDS load, issued so that the compiler does not see the LDS write.
+// The compiler otherwise makes every later LDS read wait for all outstanding buffer loads
+// (it cannot tell the stages of a ring apart), which serialises a prefetch ring. Callers own
+// the synchronisation: s_waitcnt vmcnt for their own loads, then lds_barrier().
+// The LDS address goes through M0, which the load reads when it is issued (one wait state
+// between the M0 write and the load); M0 is saved and restored around it.
+__device__ __forceinline__ void buffer_load16_lds_async(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voff) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)LDS_PTR(void, const_cast<void*>(lds_base));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(r)
+      : "memory");
+}
+
+// Workgroup barrier that is also a compiler barrier for memory accesses, without the
+// s_waitcnt vmcnt(0) / lgkmcnt(0) that __syncthreads() adds.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // s_waitcnt vmcnt(n) (n < 16), leaving the other counters alone.
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
 

@@ -19,11 +19,17 @@
 //   score tile converted to bf16 and V^T comes out of LDS through ds_read_b64_tr_b16.
 //
 // Lazy running maximum: the max m of a row moves only when needed. The fast path computes
-// p = exp2(s - m) for the tile and its sum without looking at the maximum; if some lane's
-// sum exceeds 2^10 (or is not finite, which also covers m = -inf before any visible key),
-// the wave redoes the tile with the exact maximum (S recomputed from the K tile still in
-// LDS) and rescales O. Terms are at most 2^10 on the fast path, so nothing overflows, and
-// every term of a row uses the row's current m: the softmax is unchanged.
+// p = exp2(s - m) for a tile and its sum without looking at the maximum; if some lane's
+// sum exceeds 2^32 (or is not finite, which also covers m = -inf before any visible key),
+// the wave redoes the tile with the exact maximum (S is still in registers) and rescales O.
+// bf16 P and fp32 O / d keep their relative precision at any magnitude, so the bound only
+// has to rule out overflow: terms stay below 2^32, and every term of a row uses the row's
+// current m, so the softmax is unchanged.
+//
+// Two kernels share these steps: a 4-wave kernel (window, short sequences) and an 8-wave
+// "ping-pong" kernel for long sequences (described above prefill_pp_kernel).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,7 +41,7 @@ constexpr int kTileN = 64;          // keys per tile
 constexpr int kStages = 3;          // K/V tiles in flight: the current one and two prefetched
 constexpr int kTileBytes = kTileN * kHeadDim * 2;  // 8 KB of K (or V) per tile
 constexpr int kStageBytes = 2 * kTileBytes;        // K then V
-constexpr float kSumGuard = 1024.f; // fast-path bound on a lane's tile sum of exp2(s - m)
+constexpr float kSumGuard = 4294967296.f;  // fast-path bound (2^32) on a lane's sum of exp2(s - m)
 }  // namespace
 
 template <int GP, int RB>
@@ -337,6 +343,348 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }  // pass
 }
 
+// Ping-pong variant for long sequences (no window): 8 waves per workgroup, each owning 64 rows
+// (two 32-row blocks). Waves w and w + 4 run on the same SIMD; group A (waves 0-3) and group B
+// (waves 4-7) walk the same sequence of phases one phase apart, separated by workgroup
+// barriers, so in every slot one wave of each SIMD is in a matrix phase and the other in a
+// softmax phase:
+//   matrix phase t:  O^T += V_{t-1}^T P_{t-1}^T, then S_t^T = K_t Q^T   (MFMA, LDS reads)
+//   softmax phase t: P_t = exp2(c S_t - m) with the lazy-max guard       (VALU only)
+// The softmax of one wave then runs while the other wave's MFMAs occupy the matrix unit,
+// instead of both waves alternating between the two kinds of work on their own.
+// K/V tiles (64 keys) go through a 4-stage LDS ring: tile t is read in slots 2t .. 2t + 3 and
+// is loaded (buffer loads straight into LDS) during slots 2t - 4 .. 2t - 1.
+template <int GP>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_pp_kernel(PrefillParams p) {
+  constexpr int RB = 2;
+  constexpr int NW = 8;
+  constexpr int ROWS = 64 * NW;
+  constexpr int TOK = ROWS / GP;
+  constexpr int kRing = 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[kRing][kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lag = w >> 2;  // group B runs one phase behind group A
+  const int half = lane >> 5;
+  const int r32 = lane & 31;
+
+  const int n_hg = p.hkv * (p.group / GP);
+  const int per_xcd = gridDim.x / 8;
+  const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int unit = item % p.units;
+  const int bh = item / p.units;
+  if (bh >= p.batch * n_hg) return;
+  const int b = bh / n_hg;
+  const int hg = bh - b * n_hg;
+  const int nhb = p.group / GP;
+  const int kvh = hg / nhb;
+  const int head0 = kvh * p.group + (hg - kvh * nhb) * GP;
+
+  const int q0 = clampi(p.cu_q[b], 0, p.total_q);
+  const int q1 = clampi(p.cu_q[b + 1], q0, p.total_q);
+  const int k0 = clampi(p.cu_kv[b], 0, p.total_kv);
+  const int k1 = clampi(p.cu_kv[b + 1], k0, p.total_kv);
+  const int Lq = min(q1 - q0, p.max_q);
+  const int Lk = min(k1 - k0, p.max_kv);
+  const int off = Lk - Lq;
+  const float c = p.scale_log2;
+  const int n_blk = (Lq + TOK - 1) / TOK;
+
+  const uint32_t row_bytes = (uint32_t)p.hkv * (kHeadDim * 2);
+  const size_t seq_base = (size_t)k0 * p.hkv * kHeadDim;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + seq_base, (uint32_t)Lk * row_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + seq_base, (uint32_t)Lk * row_bytes);
+
+  for (int pass = 0; pass < (p.pair_blocks ? 2 : 1); ++pass) {
+  if (pass == 0 && unit >= (p.pair_blocks ? (n_blk + 1) / 2 : n_blk)) break;
+  const int tile = (pass == 0) ? unit : n_blk - 1 - unit;
+  if (pass == 1 && tile <= unit) break;
+  const int ts = tile * TOK;
+  const int te = min(ts + TOK, Lq);
+
+  auto visible_keys = [&](int rb, int& vl, int& vh) {
+    const int pos = off + ts + ((w * RB + rb) * 32 + r32) / GP;
+    vh = p.causal ? min(Lk, pos + 1) : Lk;
+    vl = 0;
+    if (vh < vl) vh = vl;
+  };
+  u32x4 qb[RB][4];
+  float m[RB], lsum[RB];
+  f32x16 o[RB][2];
+  int hi_min = 0x7fffffff, lo_max = -0x7fffffff;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = (w * RB + rb) * 32 + r32;
+    const int t = ts + r / GP;
+    const int head = head0 + (r % GP);
+    const bool row_ok = t < te;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qb[rb][ks] = row_ok ? *reinterpret_cast<const u32x4*>(p.q + ((size_t)(q0 + t) * p.hq + head) * kHeadDim + ks * 16 + half * 8)
+                          : u32x4{0, 0, 0, 0};
+    }
+    m[rb] = (p.sinks != nullptr) ? p.sinks[head] * kLog2e : kNegInf;
+    lsum[rb] = (half == 0) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { o[rb][0][i] = 0.f; o[rb][1][i] = 0.f; }
+    int vl, vh;
+    visible_keys(rb, vl, vh);
+    if (row_ok) {
+      hi_min = min(hi_min, vh);
+      lo_max = max(lo_max, vl);
+    }
+  }
+#pragma unroll
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+    hi_min = min(hi_min, __shfl_xor(hi_min, o2, 64));
+    lo_max = max(lo_max, __shfl_xor(lo_max, o2, 64));
+  }
+  hi_min = __builtin_amdgcn_readfirstlane(hi_min);
+  lo_max = __builtin_amdgcn_readfirstlane(lo_max);
+
+  const int p_hi = off + te - 1;
+  const int jb = 0;
+  const int je = p.causal ? min(Lk, p_hi + 1) : Lk;
+  const int nt = (je > jb) ? (je - jb + kTileN - 1) / kTileN : 0;
+
+  if (nt > 0) {
+    // Wave w loads rows [8w, 8w + 8) of a tile's K and V (one 1 KB load each); lane i writes
+    // chunk position i & 7 of row i >> 3, with the same swizzles as the 4-wave kernel.
+    auto issue_tile = [&](int t) {
+      const int r = 8 * w + (lane >> 3);
+      const int pch = lane & 7;
+      const uint32_t rowoff = (uint32_t)(jb + t * kTileN + r) * row_bytes + (uint32_t)kvh * (kHeadDim * 2);
+      unsigned char* dst = kv_lds[t & (kRing - 1)] + 8 * w * 128;
+      buffer_load16_lds_async(rk, dst, rowoff + (uint32_t)((pch ^ ((r >> 1) & 7)) * 16));
+      buffer_load16_lds_async(rv, dst + kTileBytes, rowoff + (uint32_t)((pch ^ (((r >> 1) & 1) * 4)) * 16));
+    };
+    issue_tile(0);
+    if (nt > 1) issue_tile(1);
+
+    f32x16 s[RB][2];      // S^T of the current tile, per row block and 32-key half
+    u32x4 pk[RB][2][2];   // P^T as bf16 B operands, per row block, half and 16-key step
+
+    // Per-lane LDS offsets. K: row r32 of a half, 16-byte chunk (2 ks + half) ^ f(row) (f only
+    // depends on the row inside the half). V: the transposing reads of 16-key step kk start at
+    // row 16 kk + 4 (grp >> 1) + (jl >> 2); their swizzle does not depend on kk.
+    uint32_t k_off[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) k_off[ks] = r32 * 128 + (((2 * ks + half) ^ ((r32 >> 1) & 7)) << 4);
+    uint32_t v_off[2];
+    {
+      const int grp = lane >> 4;
+      const int jl = lane & 15;
+      const int krow = 4 * (grp >> 1) + (jl >> 2);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const int c0 = dt * 32 + 16 * (grp & 1) + 4 * (jl & 3);
+        v_off[dt] = krow * 128 + ((((c0 >> 3) ^ (((krow >> 1) & 1) * 4)) << 4) + ((c0 & 7) << 1));
+      }
+    }
+
+    // Matrix phase t: O^T += V_{t-1}^T P_{t-1}^T (if t >= 1), then S_t^T = K_t Q^T (if t < nt).
+    // Every LDS fragment of the phase is requested before the first MFMA.
+    auto matrix_phase = [&](int t, auto pv_tag, auto qk_tag) {
+      constexpr bool do_pv = decltype(pv_tag)::value, do_qk = decltype(qk_tag)::value;
+      // The phases of one wave stay apart: letting the scheduler hoist this phase's LDS reads
+      // into the softmax phase would keep S, P and all fragments live at once.
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 av[4][2], ka[2][4];
+      if constexpr (do_pv) {
+        const unsigned char* vt = kv_lds[(t - 1) & (kRing - 1)] + kTileBytes;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt)
+            av[kk][dt] = join_tr16(lds_read_tr16(vt + kk * 2048 + v_off[dt]), lds_read_tr16(vt + kk * 2048 + 1024 + v_off[dt]));
+      }
+      if constexpr (do_qk) {
+        const unsigned char* kt_lds = kv_lds[t & (kRing - 1)];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) ka[kt][ks] = *reinterpret_cast<const u32x4*>(kt_lds + kt * 4096 + k_off[ks]);
+      }
+      // Keep the PV products ahead of the QK products: interleaving them would keep P, S and
+      // both sets of fragments live at once.
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (do_pv) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+              o[rb][dt] = mfma32(as_bf16x8(av[kk][dt]), as_bf16x8(pk[rb][kk >> 1][kk & 1]), o[rb][dt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (do_qk) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              s[rb][kt] = mfma32(as_bf16x8(ka[kt][ks]), as_bf16x8(qb[rb][ks]), ks == 0 ? f32x16{} : s[rb][kt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto mask_half = [&](int hs, int kt) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        int vl, vh;
+        visible_keys(rb, vl, vh);
+        const unsigned span = (unsigned)(vh - vl);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = hs + 8 * (i >> 2) + 4 * half + (i & 3);
+          s[rb][kt][i] = ((unsigned)(j - vl) < span) ? s[rb][kt][i] : kNegInf;
+        }
+      }
+    };
+    auto exp_half = [&](int kt, int rb, float nm) -> float {
+      float a0, a1;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float e0 = fast_exp2(__builtin_fmaf(s[rb][kt][i], c, nm));
+        const float e1 = fast_exp2(__builtin_fmaf(s[rb][kt][i + 1], c, nm));
+        a0 = (i == 0) ? e0 : a0 + e0;
+        a1 = (i == 0) ? e1 : a1 + e1;
+        pk[rb][kt][i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
+      }
+      return a0 + a1;
+    };
+    // Softmax phase t: P_t from S_t with the lazy-max guard, taken over the whole 64-key tile:
+    // both halves are converted before the PV product of the next matrix phase, so a move of m
+    // must redo both of them (a P computed with the old m would be added to the rescaled O).
+    auto softmax_phase = [&](int t) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int hs = jb + t * kTileN + kt * 32;
+        if (!(hs >= lo_max && hs + 32 <= hi_min)) mask_half(hs, kt);
+      }
+      float ps[RB][2];
+      for (int attempt = 0; attempt < 2; ++attempt) {
+        bool ok = true;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            ps[rb][kt] = exp_half(kt, rb, (m[rb] == kNegInf && attempt > 0) ? 0.f : -m[rb]);
+            ok = ok && (ps[rb][kt] <= kSumGuard);
+          }
+        if (__builtin_expect(!__any(!ok), 1) || attempt > 0) break;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float mx = kNegInf;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[rb][0][i], s[rb][1][i]));
+          mx = fmaxf(mx, shfl_xor(mx, 32)) * c;
+          const float m_new = fmaxf(m[rb], mx);
+          const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m[rb] - m_new);
+          m[rb] = m_new;
+          lsum[rb] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) { o[rb][0][i] *= alpha; o[rb][1][i] *= alpha; }
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) lsum[rb] += ps[rb][0] + ps[rb][1];
+    };
+    // Slots: group A runs M_t in slot 2t and V_t in slot 2t + 1; group B runs one slot later.
+    // There is one workgroup barrier per tile, at the start of every even slot 2u: before it,
+    // tile u must be in LDS (tile u + 1 may still be in flight); after it, tile u + 2 goes into
+    // the stage of tile u - 2. Between two barriers (the period of tile u) group A runs
+    // M_u, V_u and group B runs V_{u-1}, M_u, so the reads of tile u - 2 all happened in
+    // earlier periods, and the two waves of a SIMD stay in opposite phases.
+    auto sync_slot = [&](int slot) {
+      if (slot & 1) return;
+      const int u = slot >> 1;
+      if (u < nt) {
+        if (u + 1 < nt) {
+          WAIT_VMCNT(2);
+        } else {
+          WAIT_VMCNT(0);
+        }
+      }
+      lds_barrier();
+      if (u + 2 < nt) issue_tile(u + 2);
+    };
+
+    // 2 nt + 3 slots for every wave (group A idles in the last one, group B in the first).
+    // The first and last matrix phases are peeled so that S is always written before it is
+    // read inside the loop (and so is dead across its back edge).
+    // Issue priorities keep the two groups in opposite phases between barriers: matrix phases
+    // first (their MFMAs then issue as soon as the matrix unit frees up), then the softmax
+    // phase that opened the period (group B's), then the one that started mid-period (group
+    // A's), which would otherwise win the VALU and push group B's softmax into the next slot.
+    auto prio_matrix = [&]() { __builtin_amdgcn_s_setprio(3); };
+    auto prio_softmax = [&]() {
+      if (lag) {
+        __builtin_amdgcn_s_setprio(2);
+      } else {
+        __builtin_amdgcn_s_setprio(1);
+      }
+    };
+    const std::true_type yes{};
+    const std::false_type no{};
+    if (lag) sync_slot(0);
+    sync_slot(lag);
+    prio_matrix();
+    matrix_phase(0, no, yes);
+    sync_slot(1 + lag);
+    prio_softmax();
+    softmax_phase(0);
+    for (int t = 1; t < nt; ++t) {
+      sync_slot(2 * t + lag);
+      prio_matrix();
+      matrix_phase(t, yes, yes);
+      sync_slot(2 * t + 1 + lag);
+      prio_softmax();
+      softmax_phase(t);
+    }
+    sync_slot(2 * nt + lag);
+    prio_matrix();
+    matrix_phase(nt, yes, no);
+    __builtin_amdgcn_s_setprio(0);
+    sync_slot(2 * nt + 1 + lag);
+    if (!lag) sync_slot(2 * nt + 2);
+    // The last loads were retired in the loop; every wave is done with the ring before the
+    // next pass reuses it.
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float lt = lsum[rb] + shfl_xor(lsum[rb], 32);
+    const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
+    const int r = (w * RB + rb) * 32 + r32;
+    const int t = ts + r / GP;
+    const int head = head0 + (r % GP);
+    if (t < te) {
+      uint16_t* orow = p.out + ((size_t)(q0 + t) * p.hq + head) * kHeadDim;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = dt * 32 + 8 * q4 + 4 * half;
+          u32x2 pkd;
+          pkd[0] = pack_bf16x2(o[rb][dt][q4 * 4 + 0] * inv, o[rb][dt][q4 * 4 + 1] * inv);
+          pkd[1] = pack_bf16x2(o[rb][dt][q4 * 4 + 2] * inv, o[rb][dt][q4 * 4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d0) = pkd;
+        }
+      }
+      if (p.lse != nullptr && half == 0) {
+        p.lse[(size_t)(q0 + t) * p.hq + head] =
+            (m[rb] == kNegInf || !(lt > 0.f)) ? kNegInf : (m[rb] + fast_log2(lt)) * kLn2;
+      }
+    }
+  }
+  }  // pass
+}
+
 namespace {
 template <int RB>
 hipError_t launch_rb(PrefillParams p, int gp, hipStream_t stream) {
@@ -352,6 +700,23 @@ hipError_t launch_rb(PrefillParams p, int gp, hipStream_t stream) {
     case 4: hipLaunchKernelGGL((prefill_kernel<4, RB>), grid, block, 0, stream, p); break;
     case 8: hipLaunchKernelGGL((prefill_kernel<8, RB>), grid, block, 0, stream, p); break;
     default: hipLaunchKernelGGL((prefill_kernel<16, RB>), grid, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pp(PrefillParams p, int gp, hipStream_t stream) {
+  const int tok = 512 / gp;
+  const int n_blk = (p.max_q + tok - 1) / tok;
+  p.pair_blocks = p.causal ? 1 : 0;
+  p.units = p.pair_blocks ? (n_blk + 1) / 2 : n_blk;
+  const long items = (long)p.units * p.batch * p.hkv * (p.group / gp);
+  dim3 grid((unsigned)(8 * ((items + 7) / 8))), block(512);
+  switch (gp) {
+    case 1: hipLaunchKernelGGL((prefill_pp_kernel<1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((prefill_pp_kernel<2>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((prefill_pp_kernel<4>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((prefill_pp_kernel<8>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((prefill_pp_kernel<16>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }
@@ -372,6 +737,8 @@ int prefill_row_blocks(int max_q, int gp) {
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (p.batch == 0 || p.total_q == 0 || p.max_q == 0) return hipSuccess;
   const int gp = prefill_heads_per_tile(p.group);
+  // long sequences without a window: the 8-wave ping-pong kernel
+  if (p.window == 0 && p.max_q >= 2048) return launch_pp(p, gp, stream);
   return prefill_row_blocks(p.max_q, gp) == 2 ? launch_rb<2>(p, gp, stream) : launch_rb<1>(p, gp, stream);
 }
 

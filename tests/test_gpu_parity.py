@@ -151,6 +151,24 @@ def test_prefill_deterministic(amd):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("hq,hkv,sinks", [(8, 1, True), (16, 16, True), (32, 2, False), (12, 3, True),
+                                           (4, 2, True)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_long_sequences(amd, hq, hkv, sinks, causal):
+    """Batches whose longest sequence has >= 2048 tokens (the 8-wave kernel without a window):
+    ragged lengths, a short sequence in the same batch, every packing of query heads per tile
+    (GQA group 1, 2, 4, 8, 16), causal and bidirectional, with and without sinks. Sampled rows
+    cover whole 64-token blocks at both ends, both wave groups and several row blocks."""
+    spec = scaled(CONFIGS["causal_prefill"], batch=3, hq=hq, hkv=hkv, causal=causal, seed=60 + hq + causal)
+    inp = make_varlen(spec, seqlens=[2100, 77, 2048 + 37])
+    out, lse = run_prefill(amd, inp, spec, sinks=sinks)
+    rows = {0: list(range(0, 70)) + [511, 512, 1023, 1500, 2047] + list(range(2030, 2100)),
+            1: list(range(77)),
+            2: [0, 31, 32, 1000] + list(range(2040, 2085))}
+    ro, rl = oracle_prefill(inp, spec, sinks=sinks, seqs=list(rows), rows=rows)
+    assert_close(out, lse, ro, rl, f"long prefill hq={hq} hkv={hkv} causal={causal}")
+
+
 @pytest.mark.parametrize("name", ["causal_prefill", "window_prefill"])
 def test_prefill_full_size_sampled(amd, name):
     spec = CONFIGS[name]
