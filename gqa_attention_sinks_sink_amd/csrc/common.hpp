@@ -52,6 +52,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+//   16x16x16: A lane l = row l%16, k 4*(l/16)+[0..3]; B lane l = col l%16, same k;
+//             C as 16x16x32.
+__device__ __forceinline__ f32x4 mfma16k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -69,6 +74,12 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* lds_addr) {
 __device__ __forceinline__ u32x4 join_tr16(s16x4 lo, s16x4 hi) {
   const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
   return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// 16-byte load of data read once (KV cache streaming): non-temporal, so it does not displace
+// reusable lines from the caches.
+__device__ __forceinline__ u32x4 load_stream(const uint16_t* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
 }
 
 // Raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes return zero
@@ -101,6 +112,33 @@ __device__ __forceinline__ void buffer_load16_lds_async(__amdgpu_buffer_rsrc_t r
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(r)
+      : "memory");
+}
+
+// Buffer resource whose base and size are taken from lane 0 (the caller guarantees they are
+// wave-uniform), so that it lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const void* ub = (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return make_rsrc(ub, __builtin_amdgcn_readfirstlane(bytes));
+}
+
+// Non-temporal variant (data read once: K/V cache streaming); lds_addr is the wave-uniform
+// LDS byte address that lane 0 writes.
+__device__ __forceinline__ void buffer_load16_lds_async_nt(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr_in, uint32_t voff) {
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(lds_addr_in);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
       "s_nop 0\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)

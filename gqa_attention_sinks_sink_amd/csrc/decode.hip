@@ -18,14 +18,23 @@
 //     scalars.
 //   * Inside an item, columns = the q_len query tokens x G query heads that share the KV
 //     head (one K/V fetch serves all of them), padded to NT tiles of 16. The chunk's keys
-//     are cut into 32-key steps dealt round-robin to the 4 waves; a step is two 16-key
-//     groups, each inside one page.
-//   * Per step: K goes from HBM straight into registers in the MFMA A layout; S^T = K Q^T
-//     with v_mfma_f32_16x16x32_bf16; masks from indices; online softmax in the exp2
-//     domain; V rows pass through LDS and come back transposed (ds_read_b64_tr_b16) as
-//     the A operand of O^T += V^T P^T.
-//   * The 4 wave states are combined in LDS in a fixed order (bit-reproducible) and the
-//     chunk partial (o/d, m + ln d) goes to the workspace at the plan's offset.
+//     are cut into 16-key groups (each inside one page: a contiguous 2 KB block of K and
+//     one of V); wave w owns groups w, w + 4, w + 8, ...
+//   * Streaming: every wave moves its own groups HBM -> LDS with non-temporal buffer loads
+//     that write LDS directly, through a private ring of S stages, so S groups are in
+//     flight per wave without holding registers, and the next item's first groups are
+//     already requested before the current item is combined. A wave only reads the LDS it
+//     filled, so the streaming needs no workgroup barrier; the compiler does not see these
+//     loads (it would otherwise wait for all of them before every LDS read) and the waits
+//     are explicit s_waitcnt vmcnt counts.
+//   * Per group: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K fragments from LDS, Q^T in
+//     registers); masks from indices; online softmax in the exp2 domain with a lazy
+//     running max; P^T (which already has the B-operand layout of the 16x16x16 product)
+//     times V^T read from LDS transposed (ds_read_b64_tr_b16): O^T += V^T P^T with
+//     v_mfma_f32_16x16x16_bf16.
+//   * The 4 wave states are combined in a fixed order ((w0 + w1) + (w2 + w3),
+//     bit-reproducible) through LDS and the chunk partial (o/d, m + ln d) goes to the
+//     workspace at the plan's offset.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,16 +44,17 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kVRowBytes = 160;               // padded LDS row of V (64 bf16 = 128 B + 32)
-constexpr int kVWaveBytes = 32 * kVRowBytes;  // 32 keys per wave step
-constexpr int kSegKeys = 1024;                // keys whose page ids one wave holds (64 lanes x 16)
-constexpr float kLazyMax = 8.0f;              // running-max slack (log2 units) before a rescale
+constexpr int kGroupKeys = 16;
+constexpr int kGroupBytes = kGroupKeys * kHeadDim * 2;  // 2 KB of K (or V) per group
+constexpr int kStageBytes = 2 * kGroupBytes;            // K then V
+constexpr int kSegGroups = 64;                          // page ids held by one lane vector
+constexpr float kLazyMax = 16.0f;                       // running-max slack (log2 units)
 
-__device__ __forceinline__ int seq_len_clamped(const DecodeParams& p, int b) {
-  int L = p.kv_lens[b];
-  int cap = p.max_kv_len < p.max_pages * p.page_size ? p.max_kv_len : p.max_pages * p.page_size;
-  return clampi(L, 0, cap);
-}
+// Ring stages per wave, by column-tile count: as deep as the LDS budget of two
+// workgroups per CU allows next to the combine buffers.
+template <int NT> struct DecodeRing { static constexpr int value = 3; };
+template <> struct DecodeRing<1> { static constexpr int value = 4; };
+template <> struct DecodeRing<4> { static constexpr int value = 2; };
 
 __device__ __forceinline__ int chunks_for(int L, int chunk) {
   int n = (L + chunk - 1) / chunk;
@@ -66,64 +76,114 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-// Element offset of the K/V row (page, kv head, slot) in the cache.
-__device__ __forceinline__ size_t cache_row(const DecodeParams& p, int page, int kvh, int slot) {
-  return (((size_t)page * p.hkv + kvh) * p.page_size + slot) * (size_t)kHeadDim;
+// LDS layout of a group: row r (key) holds 8 chunks of 16 B; chunk c sits at position
+// c ^ swz(r). K: swz = (r >> 1) & 7, so that the 16 rows read by one 16-lane group at the
+// same chunk (A operand of the 16x16x32 product) hit 64 distinct banks. V: swz flips bit 2
+// with (r >> 1) & 1 and bit 1 with (r >> 2) & 1, so that the transposing reads (4 rows x
+// 32 B per 16 lanes) of two neighbouring lane groups do not share banks.
+__device__ __forceinline__ int k_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int v_swz(int r) { return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1); }
+
+// 16 bytes HBM -> VGPRs, hidden from the compiler's wait-count tracking (the callers wait
+// with wait_vmcnt_tied before using the registers).
+__device__ __forceinline__ u32x4 load_async16(const void* ptr) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(ptr) : "memory");
+  return v;
+}
+
+// s_waitcnt vmcnt(N) (N < 64) that also orders memory accesses for the compiler.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+// vmcnt(4 k) for a runtime k in [0, 15].
+__device__ __forceinline__ void wait_groups(int k) {
+  switch (k) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<4>(); break;
+    case 2: wait_vmcnt<8>(); break;
+    case 3: wait_vmcnt<12>(); break;
+    case 4: wait_vmcnt<16>(); break;
+    case 5: wait_vmcnt<20>(); break;
+    case 6: wait_vmcnt<24>(); break;
+    default: wait_vmcnt<28>(); break;
+  }
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace
 
-// Resident waves per SIMD and steps of loads in flight per wave, per column-tile count
-// (measured on MI355X). With one tile (single-token decode) the step math is short and 4
-// waves per SIMD with one step each stream best; with more tiles the step math is longer,
-// so each wave keeps two steps in flight and the register budget sets the occupancy.
 template <int NT>
-struct DecodeOccupancy { static constexpr int value = 1; };
-template <> struct DecodeOccupancy<1> { static constexpr int value = 4; };
-template <> struct DecodeOccupancy<2> { static constexpr int value = 2; };
-template <> struct DecodeOccupancy<3> { static constexpr int value = 2; };
-template <> struct DecodeOccupancy<4> { static constexpr int value = 1; };
-template <int NT>
-constexpr int kStepsInFlight = (NT == 1) ? 1 : 2;
-
-template <int NT>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(DecodeOccupancy<NT>::value, DecodeOccupancy<NT>::value)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeParams p) {
-  // Per-wave LDS region: V staging of a step, then the wave's O^T for the combine.
-  constexpr int kWaveRegion = (kVWaveBytes > NT * 16 * kHeadDim * 4) ? kVWaveBytes : NT * 16 * kHeadDim * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * kWaveRegion];
-  __shared__ float red_m[kWaves][NT * 16];
-  __shared__ float red_l[kWaves][NT * 16];
+  constexpr int S = DecodeRing<NT>::value;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kWaves][S][kStageBytes];
+  // Combine exchange: two slots of per-lane wave states (O^T tiles, then m and d per tile).
+  __shared__ __attribute__((aligned(16))) f32x4 xo[2][NT][4][64];
+  __shared__ __attribute__((aligned(8))) float xm[2][NT][64], xl[2][NT][64];
+
+  // LDS byte address of the ring (a constant of the kernel's LDS layout)
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)LDS_PTR(unsigned char, &ring[0][0][0]);
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = p.group;
   const int R = p.q_len * G;  // live columns
   const int col_lo = lane & 15;
   const int grp = lane >> 4;  // 16-lane group 0..3
-  unsigned char* vl = lds + w * kWaveRegion;
+  const float c2 = p.scale_log2;
+
+  // Sinks of heads 0..255 in four lane vectors (one load at the start, none per item).
+  float sink_vec[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 64 * i + lane;
+    sink_vec[i] = (p.sinks != nullptr && h < p.hq) ? p.sinks[h] * kLog2e : kNegInf;
+  }
+  auto sink_of = [&](int h) -> float {
+    if (p.sinks == nullptr) return kNegInf;
+    if (h >= 256) return p.sinks[h] * kLog2e;  // more heads than the vectors hold
+    const float v0 = __shfl(sink_vec[0], h & 63, 64), v1 = __shfl(sink_vec[1], h & 63, 64);
+    const float v2 = __shfl(sink_vec[2], h & 63, 64), v3 = __shfl(sink_vec[3], h & 63, 64);
+    const int i = h >> 6;
+    return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
+  };
 
   // ---- total number of (sequence, chunk) pairs, and a cursor over sequences
+  const int cap = p.max_kv_len < p.max_pages * p.page_size ? p.max_kv_len : p.max_pages * p.page_size;
   int tot = 0;
-  for (int i = lane; i < p.batch; i += 64) tot += chunks_for(seq_len_clamped(p, i), p.kv_chunk);
+  for (int i = lane; i < p.batch; i += 64) tot += chunks_for(clampi(p.kv_lens[i], 0, cap), p.kv_chunk);
   const int total_items = wave_sum_int(tot) * p.hkv;
 
   int cur_base = 0;    // first sequence of the cursor window
   int cur_before = 0;  // pairs before cur_base
   int win_incl = 0;    // inclusive prefix of chunk counts inside the window (this lane's sequence)
+  int win_len = 0;     // clamped length of this lane's sequence
   int win_total = 0;
   auto load_window = [&]() {
     const int i = cur_base + lane;
-    const int n = (i < p.batch) ? chunks_for(seq_len_clamped(p, i), p.kv_chunk) : 0;
+    win_len = (i < p.batch) ? clampi(p.kv_lens[i], 0, cap) : 0;
+    const int n = (i < p.batch) ? chunks_for(win_len, p.kv_chunk) : 0;
     win_incl = wave_inclusive_scan(n, lane);
     win_total = __builtin_amdgcn_readlane(win_incl, 63);
   };
   load_window();
 
-  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+  struct Loc {
+    int b, c, kvh, L, n_b, base, chunk_lo, chunk_hi, n_groups;
+  };
+  // Location of an item (the cursor only moves forward: items are visited in order).
+  auto locate = [&](int item) -> Loc {
+    Loc r;
     const int P = item / p.hkv;
-    const int kvh = item - P * p.hkv;
+    r.kvh = item - P * p.hkv;
     while (P >= cur_before + win_total) {
       cur_before += win_total;
       cur_base += 64;
@@ -131,304 +191,327 @@ void decode_split_kernel(DecodeParams p) {
     }
     const unsigned long long before_mask = __ballot(cur_before + win_incl <= P);
     const int idx = __popcll(before_mask);
-    const int b = cur_base + idx;
+    r.b = cur_base + idx;
     const int pairs_before = cur_before + (idx > 0 ? __builtin_amdgcn_readlane(win_incl, idx - 1) : 0);
-    const int c = P - pairs_before;
-
-    const int L = seq_len_clamped(p, b);
-    const int n_b = chunks_for(L, p.kv_chunk);
-    const int base = pairs_before * p.q_len;  // indptr of row b*q_len
-    const int chunk_lo = c * p.kv_chunk;
-    const int chunk_hi = min(chunk_lo + p.kv_chunk, L);
-    const int* ptab = p.page_table + (size_t)b * p.max_pages;
-
-    // Page ids of up to 64 16-key groups (one per lane) for a segment of <= 1024 keys.
-    auto load_page_ids = [&](int seg_lo, int seg_hi) -> int {
-      const int j = seg_lo + 16 * lane;
-      int pg = 0;
-      if (j < seg_hi) pg = clampi(ptab[j >> p.page_shift], 0, p.num_pages - 1);
-      return pg;
-    };
-    int pid = load_page_ids(chunk_lo, min(chunk_lo + kSegKeys, chunk_hi));
-
-    // ---- Q^T as the B operand (k = head dim), one 16-column tile per nt
-    u32x4 qb[NT][2];
-    int pos[NT];  // absolute position of each lane's column (for masks)
+    r.c = P - pairs_before;
+    r.L = __builtin_amdgcn_readlane(win_len, idx);
+    r.n_b = chunks_for(r.L, p.kv_chunk);
+    r.base = pairs_before * p.q_len;  // indptr of row b*q_len
+    r.chunk_lo = r.c * p.kv_chunk;
+    r.chunk_hi = min(r.chunk_lo + p.kv_chunk, r.L);
+    r.n_groups = (r.chunk_hi > r.chunk_lo) ? (r.chunk_hi - r.chunk_lo + kGroupKeys - 1) / kGroupKeys : 0;
+    r.b = __builtin_amdgcn_readfirstlane(r.b);
+    r.c = __builtin_amdgcn_readfirstlane(r.c);
+    r.kvh = __builtin_amdgcn_readfirstlane(r.kvh);
+    r.L = __builtin_amdgcn_readfirstlane(r.L);
+    r.n_b = __builtin_amdgcn_readfirstlane(r.n_b);
+    r.base = __builtin_amdgcn_readfirstlane(r.base);
+    r.chunk_lo = __builtin_amdgcn_readfirstlane(r.chunk_lo);
+    r.chunk_hi = __builtin_amdgcn_readfirstlane(r.chunk_hi);
+    r.n_groups = __builtin_amdgcn_readfirstlane(r.n_groups);
+    return r;
+  };
+  // Raw page ids of groups [64 seg, 64 seg + 64) of an item, one per lane (lanes past the last
+  // group repeat it). The load is unconditional and its value is only touched where a group
+  // is issued (clamped there), so the wait for it does not come right after the load, when
+  // the item's first groups are still in flight.
+  auto load_page_ids = [&](const Loc& l, int seg) -> int {
+    const int g = min(64 * seg + lane, max(l.n_groups - 1, 0));
+    const int j = l.chunk_lo + kGroupKeys * g;
+    return p.page_table[(size_t)l.b * p.max_pages + (j >> p.page_shift)];
+  };
+  // Q^T as the B operand (k = head dim), one 16-column tile per nt.
+  auto load_q = [&](const Loc& l, u32x4 (&qb)[NT][2]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int col = nt * 16 + col_lo;
-      const int t = col / G, gh = col - (col / G) * G;
-      pos[nt] = L - p.q_len + t;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (col < R) {
-          const size_t off = ((size_t)(b * p.q_len + t) * p.hq + kvh * G + gh) * kHeadDim + ks * 32 + grp * 8;
-          qb[nt][ks] = *reinterpret_cast<const u32x4*>(p.q + off);
-        } else {
-          qb[nt][ks] = u32x4{0, 0, 0, 0};
-        }
-      }
+      const int cc = col < R ? col : 0;
+      const int t = cc / G, gh = cc - (cc / G) * G;
+      const uint16_t* src = p.q + ((size_t)(l.b * p.q_len + t) * p.hq + l.kvh * G + gh) * kHeadDim + grp * 8;
+      qb[nt][0] = load_async16(src);
+      qb[nt][1] = load_async16(src + 32);
     }
+  };
+  // DMA of this wave's group g of item l (page id taken from pid, the vector of the group's
+  // 64-group segment) into ring stage st. Rows past the chunk's last key read as zeros (the
+  // buffer range stops there), so masked keys multiply exact zeros.
+  auto issue_group = [&](const Loc& l, int pid, int g, int st) {
+    const int key0 = l.chunk_lo + kGroupKeys * g;
+    const int page = clampi(__builtin_amdgcn_readlane(pid, g & (kSegGroups - 1)), 0, p.num_pages - 1);
+    const size_t row0 = (((size_t)page * p.hkv + l.kvh) * p.page_size + (key0 & (p.page_size - 1))) * kHeadDim;
+    const int valid = min(kGroupKeys, l.chunk_hi - key0);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc_uniform(p.k_cache + row0, (uint32_t)valid * (kHeadDim * 2));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc_uniform(p.v_cache + row0, (uint32_t)valid * (kHeadDim * 2));
+    const uint32_t dst = ring_lds + (uint32_t)((w * S + st) * kStageBytes);
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int r = 8 * ii + (lane >> 3);
+      const int pch = lane & 7;
+      buffer_load16_lds_async_nt(rk, dst + ii * 1024, (uint32_t)(r * 128 + ((pch ^ k_swz(r)) << 4)));
+      buffer_load16_lds_async_nt(rv, dst + kGroupBytes + ii * 1024, (uint32_t)(r * 128 + ((pch ^ v_swz(r)) << 4)));
+    }
+  };
 
+  // Per-lane LDS offsets of a group's fragments.
+  const uint32_t k_off0 = col_lo * 128 + (((0 + grp) ^ k_swz(col_lo)) << 4);
+  const uint32_t k_off1 = col_lo * 128 + (((4 + grp) ^ k_swz(col_lo)) << 4);
+  uint32_t v_off[4];
+  {
+    const int vr = 4 * grp + (col_lo >> 2);  // row this lane points at
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int byte = dt * 32 + 8 * (col_lo & 3);
+      v_off[dt] = kGroupBytes + vr * 128 + ((((byte >> 4) ^ v_swz(vr))) << 4) + (byte & 15);
+    }
+  }
+
+  int ring_ctr = 0;  // ring position of this wave's next group
+  int pid_next;      // raw page ids of the next item's first segment (loaded during an item)
+  if ((int)blockIdx.x >= total_items) return;
+  Loc cur = locate(blockIdx.x);
+  int pid = load_page_ids(cur, 0);
+  asm volatile("" ::"v"(pid));  // wait for it before any group is requested
+  int pid_seg = 0;  // segment of the item whose page ids pid holds
+  u32x4 qb[NT][2];
+  load_q(cur, qb);
+  auto my_groups = [&](const Loc& l) -> int { return (l.n_groups > w) ? (l.n_groups - w + kWaves - 1) / kWaves : 0; };
+  int n_mine = my_groups(cur);
+  int n_pref = min(S, n_mine);
+  for (int k = 0; k < n_pref; ++k) issue_group(cur, pid, w + kWaves * k, (ring_ctr + k) % S);
+
+  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+    // Q of this item was requested before its first groups: wait for it (and the older loads).
+    switch (n_pref) {
+      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    }
+    // tie Q to the wait: no use of it may be scheduled above
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(qb[nt][0]), "+v"(qb[nt][1]));
+
+    // The next item is located and its page ids loaded on every iteration (the last one
+    // re-reads its own): the compiler's wait analysis does not follow branch conditions, and
+    // a conditional load would make it wait again after the next item's loads are issued.
+    const bool has_next = item + (int)gridDim.x < total_items;
+    const Loc nxt = locate(has_next ? item + (int)gridDim.x : item);
+    pid_next = load_page_ids(nxt, 0);
+
+    const int b = cur.b, c = cur.c, kvh = cur.kvh, L = cur.L;
     // ---- keys visible to each column inside this chunk: [vis_lo, vis_hi); wave-wide bounds
-    // decide whether a step needs masking at all.
+    // decide whether a group needs masking at all.
     int vis_lo[NT], vis_hi[NT];
     int hi_min = 0x7fffffff, lo_max = -0x7fffffff;
+    float m[NT], lsum[NT];
+    f32x4 o[NT][4];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      vis_hi[nt] = p.causal ? min(chunk_hi, pos[nt] + 1) : chunk_hi;
-      vis_lo[nt] = (p.window > 0) ? max(chunk_lo, pos[nt] - p.window + 1) : chunk_lo;
+      const int col = nt * 16 + col_lo;
+      const int pos = L - p.q_len + col / G;
+      vis_hi[nt] = p.causal ? min(cur.chunk_hi, pos + 1) : cur.chunk_hi;
+      vis_lo[nt] = (p.window > 0) ? max(cur.chunk_lo, pos - p.window + 1) : cur.chunk_lo;
       if (vis_hi[nt] < vis_lo[nt]) vis_hi[nt] = vis_lo[nt];
-      if (nt * 16 + col_lo < R) {
+      if (col < R) {
         hi_min = min(hi_min, vis_hi[nt]);
         lo_max = max(lo_max, vis_lo[nt]);
       }
+      // First chunk: the running max starts at the head's sink and d at 1 (held by lane group
+      // 0 so the column sum counts it once). Other chunks and waves: m = -inf (d = 1 is inert).
+      const int h = kvh * G + (col < R ? col % G : 0);
+      const float sink2 = sink_of(h);
+      m[nt] = (c == 0 && w == 0) ? sink2 : kNegInf;
+      lsum[nt] = (grp == 0) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[nt][dt] = f32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       hi_min = min(hi_min, __shfl_xor(hi_min, off, 64));
       lo_max = max(lo_max, __shfl_xor(lo_max, off, 64));
     }
-    const int vis_hi_min = hi_min, vis_lo_max = lo_max;
+    hi_min = __builtin_amdgcn_readfirstlane(hi_min);
+    lo_max = __builtin_amdgcn_readfirstlane(lo_max);
 
-    // ---- online-softmax state per lane: m (exp2 domain, same across the 4 lane groups of a
-    // column), a partial row sum, and O^T tiles (d = dt*16 + 4*grp + i, column nt*16 + col_lo).
-    float m[NT], lsum[NT];
-    f32x4 o[NT][4];
+    for (int k = 0; k < n_mine; ++k) {
+      const int g = w + kWaves * k;
+      wait_groups(min(S - 1, n_mine - 1 - k));
+      const unsigned char* st = ring[w][(ring_ctr + k) % S];
+      const int key0 = cur.chunk_lo + kGroupKeys * g;
+
+      // S^T: 16 keys x 16 columns per nt
+      const u32x4 ka0 = *reinterpret_cast<const u32x4*>(st + k_off0);
+      const u32x4 ka1 = *reinterpret_cast<const u32x4*>(st + k_off1);
+      s16x4 av[4];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int col = nt * 16 + col_lo;
-      const int h = kvh * G + (col < R ? col % G : 0);
-      // First chunk: the running max starts at the head's sink and d at 1 (held by lane group
-      // 0 so the column sum counts it once). Other chunks and waves: m = -inf (d = 1 is inert).
-      const float sink2 = (p.sinks != nullptr) ? p.sinks[h] * kLog2e : kNegInf;
-      m[nt] = (c == 0 && w == 0) ? sink2 : kNegInf;
-      lsum[nt] = (grp == 0) ? 1.0f : 0.0f;
+      for (int dt = 0; dt < 4; ++dt) av[dt] = lds_read_tr16(st + v_off[dt]);
+      f32x4 sc[NT];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[nt][dt] = f32x4{0, 0, 0, 0};
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 a = f32x4{0, 0, 0, 0};
+        a = mfma16(as_bf16x8(ka0), as_bf16x8(qb[nt][0]), a);
+        a = mfma16(as_bf16x8(ka1), as_bf16x8(qb[nt][1]), a);
+        sc[nt] = a;
+      }
+      // the ring stage is free again once its LDS reads have returned: request the group S
+      // places ahead
+      if (k + S < n_mine) {
+        wait_lgkm0();
+        const int g2 = g + kWaves * S;
+        if ((g2 >> 6) != pid_seg) {
+          // items longer than 64 groups: next segment's page ids, loaded and waited for right
+          // here (it drains this wave's loads, once per 64 groups). The load is kept out of
+          // the compiler's sight, which would otherwise wait before every group.
+          pid_seg = __builtin_amdgcn_readfirstlane(g2 >> 6);
+          const int gi = min(64 * pid_seg + lane, max(cur.n_groups - 1, 0));
+          const int32_t* src = p.page_table + (size_t)cur.b * p.max_pages + ((cur.chunk_lo + kGroupKeys * gi) >> p.page_shift);
+          asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(pid) : "v"(src) : "memory");
+        }
+        issue_group(cur, pid, g2, (ring_ctr + k + S) % S);
+      }
+
+      // ---- masks (only on groups that straddle a bound) + online softmax with a lazy max:
+      // m moves only when some score exceeds it by more than kLazyMax (log2 units); every term
+      // of a column always uses that column's current m, so the softmax is unchanged.
+      if (!(key0 + kGroupKeys <= hi_min && key0 >= lo_max)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const unsigned span = (unsigned)(vis_hi[nt] - vis_lo[nt]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 4 * grp + i;
+            sc[nt][i] = ((unsigned)(key - vis_lo[nt]) < span) ? sc[nt][i] : kNegInf;
+          }
+        }
+      }
+      bool bump = false;
+      float mx[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        mx[nt] = fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3])) * c2;
+        bump = bump || (mx[nt] > m[nt] + kLazyMax);
+      }
+      if (__any(bump)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float v = mx[nt];
+          v = fmaxf(v, shfl_xor(v, 16));
+          v = fmaxf(v, shfl_xor(v, 32));
+          const float m_new = fmaxf(m[nt], v);
+          const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m[nt] - m_new);
+          m[nt] = m_new;
+          lsum[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) o[nt][dt] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float neg_m = (m[nt] == kNegInf) ? 0.0f : -m[nt];
+        const float e0 = fast_exp2(__builtin_fmaf(sc[nt][0], c2, neg_m));
+        const float e1 = fast_exp2(__builtin_fmaf(sc[nt][1], c2, neg_m));
+        const float e2 = fast_exp2(__builtin_fmaf(sc[nt][2], c2, neg_m));
+        const float e3 = fast_exp2(__builtin_fmaf(sc[nt][3], c2, neg_m));
+        lsum[nt] += (e0 + e1) + (e2 + e3);
+        const u32x2 pw = u32x2{pack_bf16x2(e0, e1), pack_bf16x2(e2, e3)};
+        const s16x4 pb = __builtin_bit_cast(s16x4, pw);
+        // O^T += V^T P^T: A = V^T (row = head dim, k = the 4 keys of this lane group)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[nt][dt] = mfma16k16(av[dt], pb, o[nt][dt]);
+      }
     }
+    ring_ctr += n_mine;
 
-    for (int seg_lo = chunk_lo; seg_lo < chunk_hi; seg_lo += kSegKeys) {
-      const int seg_hi = min(seg_lo + kSegKeys, chunk_hi);
-      if (seg_lo != chunk_lo) pid = load_page_ids(seg_lo, seg_hi);
-      const int n_steps = (seg_hi - seg_lo + 31) / 32;
-        // ---- load: K straight to registers (row = key, k = head-dim slice), V rows for LDS.
-        // Loads are unconditional: a missing second group re-reads the first group's page and
-        // tail keys read slots of an allocated page; their scores are masked and their V rows
-        // zeroed before use.
-        auto issue_loads = [&](int s, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
-          const int j0 = seg_lo + 32 * s;
-          const bool hasB = (j0 + 16) < seg_hi;
-          const int pa = __builtin_amdgcn_readlane(pid, 2 * s);
-          const int pb = __builtin_amdgcn_readlane(pid, 2 * s + 1);
-          const size_t rA = cache_row(p, pa, kvh, j0 & (p.page_size - 1));
-          const size_t rB = hasB ? cache_row(p, pb, kvh, (j0 + 16) & (p.page_size - 1)) : rA;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            kr[ks] = *reinterpret_cast<const u32x4*>(p.k_cache + rA + (size_t)col_lo * kHeadDim + ks * 32 + grp * 8);
-            kr[2 + ks] = *reinterpret_cast<const u32x4*>(p.k_cache + rB + (size_t)col_lo * kHeadDim + ks * 32 + grp * 8);
-          }
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int krow = (lane >> 3) + 8 * ii;  // 0..31
-            const size_t rr = (krow < 16) ? rA : rB;
-            vr[ii] = *reinterpret_cast<const u32x4*>(p.v_cache + rr + (size_t)(krow & 15) * kHeadDim + (lane & 7) * 8);
-          }
-        };
-        auto run_step = [&](int s, const u32x4 (&kr)[4], u32x4 (&vr)[4]) {
-        const int j0 = seg_lo + 32 * s;
-        if (j0 + 32 > seg_hi) {
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int krow = (lane >> 3) + 8 * ii;
-            if (j0 + krow >= seg_hi) vr[ii] = u32x4{0, 0, 0, 0};  // keys past the range: exact zeros
-          }
-        }
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int krow = (lane >> 3) + 8 * ii;
-          *reinterpret_cast<u32x4*>(vl + krow * kVRowBytes + (lane & 7) * 16) = vr[ii];
-        }
-
-        // ---- S^T tiles: 16 keys x 16 columns per (group, nt)
-        f32x4 sc[NT][2];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            f32x4 a = f32x4{0, 0, 0, 0};
-            a = mfma16(as_bf16x8(kr[2 * g]), as_bf16x8(qb[nt][0]), a);
-            a = mfma16(as_bf16x8(kr[2 * g + 1]), as_bf16x8(qb[nt][1]), a);
-            sc[nt][g] = a;
-          }
-        }
-
-        // ---- masks (only on steps that straddle a bound) + online softmax update.
-        // The running max m is lazy: it moves only when some score exceeds it by more than
-        // kLazyMax (log2 units), so most steps need neither a cross-lane reduction nor a rescale
-        // of O; every term of a column always uses that column's current m, so the result is
-        // the same softmax (terms are at most 2^kLazyMax before the final division).
-        const bool full_step = (j0 + 32 <= vis_hi_min) && (j0 >= vis_lo_max);
-        if (!full_step) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const unsigned span = (unsigned)(vis_hi[nt] - vis_lo[nt]);
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int key = j0 + g * 16 + grp * 4 + i;
-                sc[nt][g][i] = ((unsigned)(key - vis_lo[nt]) < span) ? sc[nt][g][i] : kNegInf;
-              }
-            }
-          }
-        }
-        bool bump = false;
-        float mx[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          float v = fmaxf(fmaxf(sc[nt][0][0], sc[nt][0][1]), fmaxf(sc[nt][0][2], sc[nt][0][3]));
-          v = fmaxf(v, fmaxf(fmaxf(sc[nt][1][0], sc[nt][1][1]), fmaxf(sc[nt][1][2], sc[nt][1][3])));
-          mx[nt] = v * p.scale_log2;
-          bump = bump || (mx[nt] > m[nt] + kLazyMax);
-        }
-        if (__any(bump)) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            float v = mx[nt];
-            v = fmaxf(v, shfl_xor(v, 16));
-            v = fmaxf(v, shfl_xor(v, 32));
-            const float m_new = fmaxf(m[nt], v);
-            const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m[nt] - m_new);
-            m[nt] = m_new;
-            lsum[nt] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[nt][dt] *= alpha;
-          }
-        }
-        bf16x8 pbf[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const float neg_m = (m[nt] == kNegInf) ? 0.0f : -m[nt];
-          float ps = 0.f;
-          uint32_t packed[4];
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            float e[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              e[i] = fast_exp2(__builtin_fmaf(sc[nt][g][i], p.scale_log2, neg_m));
-              ps += e[i];
-            }
-            packed[g * 2 + 0] = pack_bf16x2(e[0], e[1]);
-            packed[g * 2 + 1] = pack_bf16x2(e[2], e[3]);
-          }
-          lsum[nt] += ps;
-          pbf[nt] = as_bf16x8(u32x4{packed[0], packed[1], packed[2], packed[3]});
-        }
-
-        // ---- O^T += V^T P^T. A operand (V^T): lane = d (dt*16 + col_lo), k slots 0..3 =
-        // group A keys 4*grp..+3, slots 4..7 = group B keys 4*grp..+3 (the P layout above).
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int rsel = grp * 4 + (col_lo >> 2);
-          const int csel = dt * 16 + 4 * (col_lo & 3);
-          const s16x4 lo = lds_read_tr16(vl + rsel * kVRowBytes + csel * 2);
-          const s16x4 hi = lds_read_tr16(vl + (16 + rsel) * kVRowBytes + csel * 2);
-          const u32x4 av = join_tr16(lo, hi);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma16(as_bf16x8(av), pbf[nt], o[nt][dt]);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        };
-
-        // This wave owns steps w, w + 4, w + 8, ... of the segment, with two steps in
-        // flight (ping-pong register buffers): the loads of step k + 1 are issued before
-        // step k is computed.
-        const int n_mine = (w < n_steps) ? (n_steps - w + kWaves - 1) / kWaves : 0;
-        if constexpr (kStepsInFlight<NT> == 1) {
-          for (int k = 0; k < n_mine; ++k) {
-            u32x4 kA[4], vA[4];
-            issue_loads(w + kWaves * k, kA, vA);
-            run_step(w + kWaves * k, kA, vA);
-          }
-        } else {
-          // The steady-state loop issues its loads unconditionally, so the compiler waits for
-          // exactly the older step's loads (a conditional load makes it wait for all of them).
-          u32x4 kA[4], vA[4], kB[4], vB[4];
-          int k = 0;
-          if (n_mine > 0) issue_loads(w, kA, vA);
-          for (; k + 2 < n_mine; k += 2) {
-            issue_loads(w + kWaves * (k + 1), kB, vB);
-            run_step(w + kWaves * k, kA, vA);
-            issue_loads(w + kWaves * (k + 2), kA, vA);
-            run_step(w + kWaves * (k + 1), kB, vB);
-          }
-          if (k + 1 < n_mine) {
-            issue_loads(w + kWaves * (k + 1), kB, vB);
-            run_step(w + kWaves * k, kA, vA);
-            run_step(w + kWaves * (k + 1), kB, vB);
-          } else if (k < n_mine) {
-            run_step(w + kWaves * k, kA, vA);
-          }
-        }
+    // ---- the next item's Q and first groups go out before this item is combined
+    int n_mine_next = 0, n_pref_next = 0;
+    if (has_next) {
+      n_mine_next = my_groups(nxt);
+      n_pref_next = min(S, n_mine_next);
     }
 
     // ---- plan: chunk counts and partial offsets (one writer per sequence)
     if (c == 0 && kvh == 0 && w == 0) {
       if (lane < p.q_len) {
-        p.counts[b * p.q_len + lane] = n_b;
-        p.indptr[b * p.q_len + lane] = base + lane * n_b;
+        p.counts[b * p.q_len + lane] = cur.n_b;
+        p.indptr[b * p.q_len + lane] = cur.base + lane * cur.n_b;
       }
-      if (b == p.batch - 1 && lane == 0) p.indptr[p.batch * p.q_len] = base + p.q_len * n_b;
+      if (b == p.batch - 1 && lane == 0) p.indptr[p.batch * p.q_len] = cur.base + p.q_len * cur.n_b;
     }
 
-    // ---- combine the 4 wave states of this chunk. Each wave leaves its (m, d) per column and
-    // its unnormalised O^T in its own LDS region (which held its V staging); after one
-    // barrier every thread merges 4 columns x 4 head-dim values over the waves in a fixed
-    // order (bit-reproducible) and writes the chunk partial: o_c = O / d, lse_c = m + ln d.
+    // ---- combine the 4 wave states in the order (w0 + w1) + (w2 + w3); each lane holds the
+    // same (column, head-dim) slots in every wave. Column sums first.
+    float lt[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float lt = lsum[nt];
-      lt += shfl_xor(lt, 16);
-      lt += shfl_xor(lt, 32);
-      if (grp == 0) {
-        red_m[w][nt * 16 + col_lo] = m[nt];
-        red_l[w][nt * 16 + col_lo] = lt;
-      }
-      float* slot = reinterpret_cast<float*>(vl);  // [NT*16 columns][64 d]
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        *reinterpret_cast<f32x4*>(&slot[(nt * 16 + col_lo) * kHeadDim + dt * 16 + grp * 4]) = o[nt][dt];
+      lt[nt] = lsum[nt];
+      lt[nt] += shfl_xor(lt[nt], 16);
+      lt[nt] += shfl_xor(lt[nt], 32);
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < R * (kHeadDim / 4); i += kThreads) {
-      const int col = i / (kHeadDim / 4);
-      const int d4 = (i % (kHeadDim / 4)) * 4;
-      float M = kNegInf;
+    auto put = [&](int slot) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww][col]);
-      const float Mu = (M == kNegInf) ? 0.f : M;
-      float Lt = 0.f;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float sc = fast_exp2(red_m[ww][col] - Mu);
-        Lt += red_l[ww][col] * sc;
-        const float* slot = reinterpret_cast<const float*>(lds + ww * kWaveRegion);
-        acc += *reinterpret_cast<const f32x4*>(&slot[col * kHeadDim + d4]) * sc;
+        for (int dt = 0; dt < 4; ++dt) xo[slot][nt][dt][lane] = o[nt][dt];
+        xm[slot][nt][lane] = m[nt];
+        xl[slot][nt][lane] = lt[nt];
       }
-      const float inv = (Lt > 0.f) ? 1.0f / Lt : 0.f;
-      const int t = col / G, gh = col % G;
-      const int pidx = base + t * n_b + c;
-      const int h = kvh * G + gh;
-      *reinterpret_cast<f32x4*>(p.o_part + ((size_t)pidx * p.hq + h) * kHeadDim + d4) = acc * inv;
-      if (d4 == 0) p.lse_part[(size_t)pidx * p.hq + h] = (M == kNegInf || !(Lt > 0.f)) ? kNegInf : (M + fast_log2(Lt)) * kLn2;
+    };
+    auto fold = [&](int slot) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float m2 = xm[slot][nt][lane], l2 = xl[slot][nt][lane];
+        const float M = fmaxf(m[nt], m2);
+        const float Mu = (M == kNegInf) ? 0.f : M;
+        const float a1 = fast_exp2(m[nt] - Mu), a2 = fast_exp2(m2 - Mu);
+        lt[nt] = lt[nt] * a1 + l2 * a2;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[nt][dt] = o[nt][dt] * a1 + xo[slot][nt][dt][lane] * a2;
+        m[nt] = M;
+      }
+    };
+    // The next item's DMAs are issued first (their ring stages are free: every group of this
+    // item has been consumed).
+    // The page-id load is compiler-visible: make its wait (a vmcnt(0), free here since every
+    // group of this item has arrived) happen before the next Q loads are issued.
+    asm volatile("" ::"v"(pid_next));
+    if (has_next) {
+      load_q(nxt, qb);
+      for (int k = 0; k < n_pref_next; ++k) issue_group(nxt, pid_next, w + kWaves * k, (ring_ctr + k) % S);
     }
-    __syncthreads();  // the LDS regions and red_* are reused by the next item
+    if (w == 1 || w == 3) put(w >> 1);
+    wait_lgkm0();
+    lds_barrier();
+    if (w == 0 || w == 2) fold(w >> 1);
+    if (w == 2) put(1);
+    wait_lgkm0();
+    lds_barrier();
+    if (w == 0) {
+      fold(1);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = nt * 16 + col_lo;
+        if (col < R) {
+          const float inv = (lt[nt] > 0.f) ? 1.0f / lt[nt] : 0.f;
+          const int t = col / G, gh = col % G;
+          const int pidx = cur.base + t * cur.n_b + c;
+          const int h = kvh * G + gh;
+          float* dst = p.o_part + ((size_t)pidx * p.hq + h) * kHeadDim + 4 * grp;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(dst + dt * 16) = o[nt][dt] * inv;
+          if (grp == 0)
+            p.lse_part[(size_t)pidx * p.hq + h] =
+                (m[nt] == kNegInf || !(lt[nt] > 0.f)) ? kNegInf : (m[nt] + fast_log2(lt[nt])) * kLn2;
+        }
+      }
+    }
+    // slot 0 is read by wave 0 before the second barrier and written by wave 1 only after the
+    // next item's groups; slot 1 is written by wave 2 after the next item's first barrier.
+    cur = nxt;
+    pid = pid_next;
+    pid_seg = 0;
+    n_mine = n_mine_next;
+    n_pref = n_pref_next;
   }
 }
 
