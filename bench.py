@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="paged_decode",
                     choices=["paged_decode", "verify", "causal_prefill", "window_prefill", "embed", "tiny_causal"])
+    ap.add_argument("--kv-chunk", type=int, default=None,
+                    help="split-KV chunk length for the paged workloads (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU oracle sample (wall seconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
@@ -244,6 +246,9 @@ def pairs_visible(L, causal, window):
 
 def bench_paged(args, torch, amd, name):
     spec = CONFIGS[name]
+    if args.kv_chunk is not None:
+        import dataclasses
+        spec = dataclasses.replace(spec, kv_chunk=args.kv_chunk)
     inp = make_paged(spec)
     dev = torch.device("cuda:0")
     q = tbits(torch, inp["q"], dev)

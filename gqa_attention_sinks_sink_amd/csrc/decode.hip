@@ -53,7 +53,7 @@ constexpr float kLazyMax = 16.0f;                       // running-max slack (lo
 // Ring stages per wave, by column-tile count: as deep as the LDS budget of two
 // workgroups per CU allows next to the combine buffers.
 template <int NT> struct DecodeRing { static constexpr int value = 3; };
-template <> struct DecodeRing<1> { static constexpr int value = 4; };
+template <> struct DecodeRing<1> { static constexpr int value = 3; };
 template <> struct DecodeRing<4> { static constexpr int value = 2; };
 
 __device__ __forceinline__ int chunks_for(int L, int chunk) {

@@ -215,7 +215,7 @@ def oracle_decode(inp, spec, seqs=None, sinks=True):
 @pytest.mark.parametrize("q_len,hq,hkv", [(1, 16, 2), (1, 64, 8), (5, 16, 2), (2, 8, 1), (8, 64, 8), (3, 4, 4),
                                           (1, 64, 1)])
 def test_decode_small(amd, q_len, hq, hkv):
-    spec = scaled(CONFIGS["verify"], batch=5, q_len=q_len, kv_len=(1, 1500), hq=hq, hkv=hkv, seed=50 + q_len + hq)
+    spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=5, q_len=q_len, kv_len=(1, 1500), hq=hq, hkv=hkv, seed=50 + q_len + hq)
     inp = make_paged(spec, kv_lens=[1500, 513, 512, 17, 8 if q_len <= 8 else q_len])
     out, lse = run_decode(amd, dev_paged(inp), inp, spec)
     ro, rl = oracle_decode(inp, spec)
@@ -224,7 +224,7 @@ def test_decode_small(amd, q_len, hq, hkv):
 
 @pytest.mark.parametrize("window", [1, 100, 600])
 def test_decode_window(amd, window):
-    spec = scaled(CONFIGS["verify"], batch=4, kv_len=(1, 2000), hq=16, hkv=2, window=window, seed=60)
+    spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=4, kv_len=(1, 2000), hq=16, hkv=2, window=window, seed=60)
     inp = make_paged(spec)
     out, lse = run_decode(amd, dev_paged(inp), inp, spec)
     ro, rl = oracle_decode(inp, spec)
@@ -232,7 +232,7 @@ def test_decode_window(amd, window):
 
 
 def test_decode_edge_lengths_and_no_sink(amd):
-    spec = scaled(CONFIGS["verify"], batch=5, kv_len=(0, 700), hq=16, hkv=2, seed=61)
+    spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=5, kv_len=(0, 700), hq=16, hkv=2, seed=61)
     inp = make_paged(spec, kv_lens=[0, 3, 5, 700, 16], max_pages_per_seq=44)
     d = dev_paged(inp)
     for sinks in (True, False):
@@ -252,7 +252,7 @@ def test_decode_page_and_chunk_sizes(amd, page_size, chunk):
 
 
 def test_decode_plan_is_bit_exact_and_partials_match(amd):
-    spec = scaled(CONFIGS["verify"], batch=6, kv_len=(1, 1800), hq=16, hkv=2, seed=63)
+    spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=6, kv_len=(1, 1800), hq=16, hkv=2, seed=63)
     inp = make_paged(spec, kv_lens=[1800, 1, 512, 513, 0, 1024])
     d = dev_paged(inp)
     need = amd.attn_sink_decode_workspace_size(6, spec.q_len, inp["max_kv_len"], spec.hq, 64, spec.kv_chunk)
@@ -275,7 +275,7 @@ def test_decode_plan_is_bit_exact_and_partials_match(amd):
 
 
 def test_merge_kernel_on_oracle_partials(amd):
-    spec = scaled(CONFIGS["verify"], batch=4, kv_len=(1, 1600), hq=8, hkv=2, seed=64)
+    spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=4, kv_len=(1, 1600), hq=8, hkv=2, seed=64)
     inp = make_paged(spec, kv_lens=[1600, 2, 700, 0])
     o_p, l_p, counts, indptr = oracle.split_decode(f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"]),
                                                    inp["page_table"], inp["kv_lens"], inp["sinks"], spec.q_len,
@@ -298,7 +298,7 @@ def test_merge_all_empty_rows(amd):
 
 
 def test_page_permutation_bit_identical(amd):
-    spec = scaled(CONFIGS["verify"], batch=4, kv_len=(50, 1200), hq=16, hkv=2, seed=65)
+    spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=4, kv_len=(50, 1200), hq=16, hkv=2, seed=65)
     inp = make_paged(spec)
     a = run_decode(amd, dev_paged(inp), inp, spec)
     perm = np.random.default_rng(3).permutation(inp["num_pages"])
@@ -332,7 +332,7 @@ def test_gqa_matches_repeated_mha(amd):
 
 
 def test_decode_deterministic(amd):
-    spec = scaled(CONFIGS["verify"], batch=3, kv_len=(100, 2000), hq=64, hkv=8, seed=68)
+    spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=3, kv_len=(100, 2000), hq=64, hkv=8, seed=68)
     inp = make_paged(spec)
     d = dev_paged(inp)
     a = run_decode(amd, d, inp, spec)
@@ -354,7 +354,7 @@ def test_decode_full_size(amd, name):
 # graph capture: launches depend on host scalars only, so calls can be captured and replayed
 # -------------------------------------------------------------------------------------------
 def test_graph_capture_replays_match_eager(amd):
-    spec = scaled(CONFIGS["verify"], batch=4, kv_len=(100, 1500), hq=16, hkv=2, seed=69)
+    spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=4, kv_len=(100, 1500), hq=16, hkv=2, seed=69)
     inp = make_paged(spec)
     d = dev_paged(inp)
     need = amd.attn_sink_decode_workspace_size(4, spec.q_len, inp["max_kv_len"], spec.hq, 64, spec.kv_chunk)
