@@ -101,13 +101,26 @@ def _pmc_per_dispatch(directory, counter):
     return vals
 
 
+def prefill_kernel_name(spec, max_seqlen):
+    """The prefill kernel the library launches for this shape (8-wave ping-pong kernel for
+    sequences of 2048+ tokens without a window, else the 4-wave kernel)."""
+    return "prefill_pp_kernel" if (spec.window <= 0 and max_seqlen >= 2048) else "prefill_kernel"
+
+
+def dominant_kernel(name):
+    if name in ("paged_decode", "verify"):
+        return "decode_split_kernel"
+    spec = CONFIGS["embed_sink" if name == "embed" else name]
+    return prefill_kernel_name(spec, spec.seqlen[1])
+
+
 def record_traffic(name, kind, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     """HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB
     per dispatch), each scaled so that a plain 1 GiB device copy reads and writes 1 GiB."""
-    kernel = "decode_split_kernel" if kind == "decode" else "prefill_kernel"
+    kernel = dominant_kernel(name)
 
     def mean_for(directory, counter, pattern):
-        v = [val for (k, val) in _pmc_per_dispatch(directory, counter).values() if pattern in k]
+        v = [val for (k, val) in _pmc_per_dispatch(directory, counter).values() if ("::" + pattern + "<") in k]
         if not v:
             raise SystemExit(f"no {counter} dispatch of {pattern} under {directory}")
         return float(np.mean(v)), len(v)
@@ -276,7 +289,12 @@ def bench_paged(args, torch, amd, name):
     flops = int((L * hkv).sum() * (hq // hkv) * ql * 4 * 64)
 
     ms = time_calls(torch, step, args.steps, args.warmup)
-    # merge kernel alone on the same partials -> split-KV kernel time = call - merge
+    # the split-KV kernel alone (the split-only entry point: the same kernel, no merge)
+    def split_only():
+        amd.attn_sink_decode_paged_partials(q, kc, vc, table, lens, sinks, ql, inp["max_kv_len"], spec.scale,
+                                            spec.causal, spec.window, spec.kv_chunk, workspace=ws)
+    split_ms = time_calls(torch, split_only, args.steps, args.warmup)
+    # merge kernel alone on the same partials
     lay = amd.decode_workspace_layout(B, ql, inp["max_kv_len"], hq, spec.kv_chunk, spec.page_size)
     n_p = lay["partials"]
     o_p = ws[lay["off_o"]:lay["off_o"] + 4 * n_p * hq * 64].view(torch.float32).view(n_p, hq, 64)
@@ -285,7 +303,6 @@ def bench_paged(args, torch, amd, name):
     out2 = torch.empty_like(out)
     merge_ms = time_calls(torch, lambda: amd.attn_sink_merge_partials(o_p, l_p, indptr, out=out2, return_lse=False),
                           args.steps, args.warmup)
-    split_ms = max(ms - merge_ms, 1e-6)
     cold_ms = None
     if not args.no_cold:
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -357,10 +374,10 @@ def bench_varlen(args, torch, amd, name):
     ai = flops / algo_bytes
     bound = "mfma" if ai > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm"
     if bound == "mfma":
-        roof = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(flops / len(specs) / (kernel_ms * 1e-3) / 1e12, 2),
+        roof = {"kernel": prefill_kernel_name(spec, mx), "bound": "mfma", "achieved": round(flops / len(specs) / (kernel_ms * 1e-3) / 1e12, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     else:
-        roof = {"kernel": "prefill_kernel", "bound": "hbm", "achieved": round(io_bytes / (kernel_ms * 1e-3) / 1e9, 1),
+        roof = {"kernel": prefill_kernel_name(spec, mx), "bound": "hbm", "achieved": round(io_bytes / (kernel_ms * 1e-3) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(name, "prefill")

@@ -18,14 +18,15 @@ import torch
 from .build import LIB_LOAD_PATH as LIB_PATH
 
 __all__ = [
-    "lib", "AttnSinkError", "attn_sink_prefill", "attn_sink_decode_paged", "attn_sink_decode_workspace_size",
+    "lib", "AttnSinkError", "attn_sink_prefill", "attn_sink_decode_paged", "attn_sink_decode_paged_partials",
+    "attn_sink_decode_workspace_size",
     "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version", "decode_workspace_layout",
     "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
-    "attn_sink_prefill", "attn_sink_decode_paged", "attn_sink_decode_workspace_size",
-    "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version",
+    "attn_sink_prefill", "attn_sink_decode_paged", "attn_sink_decode_paged_partials",
+    "attn_sink_decode_workspace_size", "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -43,6 +44,9 @@ lib.attn_sink_prefill.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _i32
 lib.attn_sink_decode_paged.restype = ctypes.c_int
 lib.attn_sink_decode_paged.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz, _vp, _fp, _vp]
+lib.attn_sink_decode_paged_partials.restype = ctypes.c_int
+lib.attn_sink_decode_paged_partials.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _i32, _i32, _i32, _i32,
+                                                _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz, _vp]
 lib.attn_sink_decode_workspace_size.restype = _sz
 lib.attn_sink_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 lib.attn_sink_merge_partials.restype = ctypes.c_int
@@ -165,14 +169,7 @@ def decode_workspace_layout(batch: int, q_len: int, max_kv_len: int, num_q_heads
                 off_lse=off_lse, total=off_lse + a(4 * partials * num_q_heads))
 
 
-def attn_sink_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,
-                           kv_lens: torch.Tensor, sinks: Optional[torch.Tensor], q_len: int, max_kv_len: int,
-                           softmax_scale: Optional[float] = None, causal: bool = True, window: int = 0,
-                           kv_chunk: int = 512, workspace: Optional[torch.Tensor] = None,
-                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                           return_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """q [batch*q_len, hq, 64]; caches [num_pages, hkv, page_size, 64] bf16; page_table int32 [batch, max_pages];
-    kv_lens int32 [batch]; workspace uint8 (allocated if None)."""
+def _decode_args(q, k_cache, v_cache, page_table, kv_lens, sinks, q_len, workspace, kv_chunk, max_kv_len):
     dev = q.device
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _check(t, n, torch.bfloat16, dev)
@@ -184,7 +181,6 @@ def attn_sink_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         raise ValueError(f"expected q [rows, hq, d] and caches [pages, hkv, page_size, d]; got {tuple(q.shape)}, "
                          f"{tuple(k_cache.shape)}, {tuple(v_cache.shape)}")
     rows, hq, d = q.shape
-    num_pages, hkv, page_size = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
     batch = kv_lens.numel()
     if rows != batch * q_len:
         raise ValueError(f"q has {rows} rows, expected batch*q_len = {batch * q_len}")
@@ -192,6 +188,25 @@ def attn_sink_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         raise ValueError(f"page_table must be [{batch}, max_pages_per_seq]")
     if sinks is not None and sinks.numel() != hq:
         raise ValueError(f"sinks must have {hq} entries")
+    if workspace is not None:
+        _check(workspace, "workspace", workspace.dtype, dev)
+    need = attn_sink_decode_workspace_size(batch, q_len, max_kv_len, hq, d, kv_chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    return batch, rows, hq, d, workspace
+
+
+def attn_sink_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,
+                           kv_lens: torch.Tensor, sinks: Optional[torch.Tensor], q_len: int, max_kv_len: int,
+                           softmax_scale: Optional[float] = None, causal: bool = True, window: int = 0,
+                           kv_chunk: int = 512, workspace: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           return_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """q [batch*q_len, hq, 64]; caches [num_pages, hkv, page_size, 64] bf16; page_table int32 [batch, max_pages];
+    kv_lens int32 [batch]; workspace uint8 (allocated if None)."""
+    batch, rows, hq, d, workspace = _decode_args(q, k_cache, v_cache, page_table, kv_lens, sinks, q_len, workspace,
+                                                 kv_chunk, max_kv_len)
+    dev = q.device
     if out is not None:
         _check(out, "out", torch.bfloat16, dev)
         if out.shape != q.shape:
@@ -200,17 +215,13 @@ def attn_sink_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         _check(lse, "lse", torch.float32, dev)
         if lse.shape != (rows, hq):
             raise ValueError(f"lse must be [{rows}, {hq}]")
-    if workspace is not None:
-        _check(workspace, "workspace", workspace.dtype, dev)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    need = attn_sink_decode_workspace_size(batch, q_len, max_kv_len, hq, d, kv_chunk)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((rows, hq), dtype=torch.float32, device=dev)
+    num_pages, hkv, page_size = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
     st = lib.attn_sink_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), page_table.shape[1],
                                     num_pages, _ptr(kv_lens), _ptr(sinks), batch, q_len, int(max_kv_len), hq, hkv, d,
                                     page_size, float(softmax_scale), int(bool(causal)), int(window), int(kv_chunk),
@@ -218,6 +229,37 @@ def attn_sink_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                     _ptr(lse), _stream(stream))
     _raise(st, "attn_sink_decode_paged")
     return out, lse
+
+
+def attn_sink_decode_paged_partials(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                    page_table: torch.Tensor, kv_lens: torch.Tensor, sinks: Optional[torch.Tensor],
+                                    q_len: int, max_kv_len: int, softmax_scale: Optional[float] = None,
+                                    causal: bool = True, window: int = 0, kv_chunk: int = 512,
+                                    workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """The split-KV pass alone. Returns views of the workspace: partial_indptr int32 [rows+1], chunk_counts
+    int32 [rows], o_partial fp32 [P, hq, 64], lse_partial fp32 [P, hq] (P = rows x chunk bound), ready for
+    attn_sink_merge_partials; plus the workspace itself."""
+    batch, rows, hq, d, workspace = _decode_args(q, k_cache, v_cache, page_table, kv_lens, sinks, q_len, workspace,
+                                                 kv_chunk, max_kv_len)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    num_pages, hkv, page_size = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    st = lib.attn_sink_decode_paged_partials(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                             page_table.shape[1], num_pages, _ptr(kv_lens), _ptr(sinks), batch, q_len,
+                                             int(max_kv_len), hq, hkv, d, page_size, float(softmax_scale),
+                                             int(bool(causal)), int(window), int(kv_chunk), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise(st, "attn_sink_decode_paged_partials")
+    lay = decode_workspace_layout(batch, q_len, int(max_kv_len), hq, kv_chunk, page_size)
+    ws = workspace.view(torch.uint8).reshape(-1)
+    n_p = lay["partials"]
+    return dict(
+        workspace=workspace,
+        partial_indptr=ws[:4 * (rows + 1)].view(torch.int32),
+        chunk_counts=ws[lay["off_counts"]:lay["off_counts"] + 4 * rows].view(torch.int32),
+        o_partial=ws[lay["off_o"]:lay["off_o"] + 4 * n_p * hq * d].view(torch.float32).view(n_p, hq, d),
+        lse_partial=ws[lay["off_lse"]:lay["off_lse"] + 4 * n_p * hq].view(torch.float32).view(n_p, hq),
+    )
 
 
 def attn_sink_merge_partials(o_partial: torch.Tensor, lse_partial: torch.Tensor, partial_indptr: torch.Tensor,

@@ -133,13 +133,18 @@ size_t attn_sink_decode_workspace_size(int32_t batch, int32_t q_len, int32_t max
   return l.total;
 }
 
-attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                                        const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
-                                        const int32_t* kv_lens, const float* sinks, int32_t batch, int32_t q_len,
-                                        int32_t max_kv_len, int32_t num_q_heads, int32_t num_kv_heads,
-                                        int32_t head_dim, int32_t page_size, float softmax_scale, int32_t causal,
-                                        int32_t window, int32_t kv_chunk, void* workspace, size_t workspace_bytes,
-                                        void* out, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+// Validation and parameters shared by the decode entry points. out_required: the call also
+// merges (out must be given).
+attn_sink_status decode_prepare(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
+                                int32_t max_pages_per_seq, int32_t num_pages, const int32_t* kv_lens,
+                                const float* sinks, int32_t batch, int32_t q_len, int32_t max_kv_len,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                float softmax_scale, int32_t causal, int32_t window, int32_t kv_chunk,
+                                void* workspace, size_t workspace_bytes, const void* out, bool out_required,
+                                DecodeParams* pp, DecodeLayout* lp) {
   if (batch < 0 || max_kv_len < 0 || max_pages_per_seq < 1 || num_pages < 1 || q_len < 1) return ATTN_SINK_ERR_INVALID_ARG;
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return ATTN_SINK_ERR_INVALID_ARG;
   if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_SINK_ERR_INVALID_ARG;
@@ -154,9 +159,10 @@ attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, cons
   DecodeLayout lay;
   if (!decode_layout(batch, q_len, max_kv_len, num_q_heads, chunk, &lay)) return ATTN_SINK_ERR_UNSUPPORTED;
   if (lay.chunks * batch * num_kv_heads > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
+  *lp = lay;
   if (batch == 0) return ATTN_SINK_OK;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || page_table == nullptr || kv_lens == nullptr ||
-      out == nullptr || workspace == nullptr)
+      (out_required && out == nullptr) || workspace == nullptr)
     return ATTN_SINK_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_SINK_ERR_INVALID_ARG;
   if (workspace_bytes < attn_sink_decode_workspace_size(batch, q_len, max_kv_len, num_q_heads, head_dim, kv_chunk) ||
@@ -164,7 +170,7 @@ attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, cons
     return ATTN_SINK_ERR_WORKSPACE_TOO_SMALL;
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  DecodeParams p;
+  DecodeParams& p = *pp;
   p.q = static_cast<const uint16_t*>(q);
   p.k_cache = static_cast<const uint16_t*>(k_cache);
   p.v_cache = static_cast<const uint16_t*>(v_cache);
@@ -189,6 +195,26 @@ attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, cons
   p.causal = causal != 0;
   p.window = window > 0 ? window : 0;
   p.scale_log2 = softmax_scale * kLog2e;
+  return ATTN_SINK_OK;
+}
+}  // namespace
+
+extern "C" {
+
+attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+                                        const int32_t* kv_lens, const float* sinks, int32_t batch, int32_t q_len,
+                                        int32_t max_kv_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t page_size, float softmax_scale, int32_t causal,
+                                        int32_t window, int32_t kv_chunk, void* workspace, size_t workspace_bytes,
+                                        void* out, float* lse, void* stream) {
+  DecodeParams p;
+  DecodeLayout lay;
+  const attn_sink_status st = decode_prepare(q, k_cache, v_cache, page_table, max_pages_per_seq, num_pages, kv_lens,
+                                             sinks, batch, q_len, max_kv_len, num_q_heads, num_kv_heads, head_dim,
+                                             page_size, softmax_scale, causal, window, kv_chunk, workspace,
+                                             workspace_bytes, out, true, &p, &lay);
+  if (st != ATTN_SINK_OK || batch == 0) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = launch_decode_split(p, (int)lay.chunks, s);
   if (e != hipSuccess) return ATTN_SINK_ERR_HIP;
@@ -203,6 +229,24 @@ attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, cons
   mp.rows = (int)lay.rows;
   mp.hq = num_q_heads;
   return hip_status(launch_merge(mp, s));
+}
+
+attn_sink_status attn_sink_decode_paged_partials(const void* q, const void* k_cache, const void* v_cache,
+                                                 const int32_t* page_table, int32_t max_pages_per_seq,
+                                                 int32_t num_pages, const int32_t* kv_lens, const float* sinks,
+                                                 int32_t batch, int32_t q_len, int32_t max_kv_len,
+                                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                 int32_t page_size, float softmax_scale, int32_t causal,
+                                                 int32_t window, int32_t kv_chunk, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  DecodeParams p;
+  DecodeLayout lay;
+  const attn_sink_status st = decode_prepare(q, k_cache, v_cache, page_table, max_pages_per_seq, num_pages, kv_lens,
+                                             sinks, batch, q_len, max_kv_len, num_q_heads, num_kv_heads, head_dim,
+                                             page_size, softmax_scale, causal, window, kv_chunk, workspace,
+                                             workspace_bytes, nullptr, false, &p, &lay);
+  if (st != ATTN_SINK_OK || batch == 0) return st;
+  return hip_status(launch_decode_split(p, (int)lay.chunks, reinterpret_cast<hipStream_t>(stream)));
 }
 
 attn_sink_status attn_sink_merge_partials(const float* o_partial, const float* lse_partial, int32_t num_partials,

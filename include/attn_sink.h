@@ -147,6 +147,22 @@ attn_sink_status attn_sink_decode_paged(
     void* out, float* lse, void* stream);
 
 /*
+ * The split-KV pass of attn_sink_decode_paged alone: writes the plan and the chunk partials
+ * into the workspace (layout above) and does not merge them. Arguments, constraints and
+ * error codes as for attn_sink_decode_paged, without out and lse. For callers that merge
+ * later, e.g. after exchanging partials of different KV ranges between devices (the merge
+ * is then attn_sink_merge_partials over partial_indptr). Enqueues one kernel.
+ */
+attn_sink_status attn_sink_decode_paged_partials(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    const int32_t* kv_lens, const float* sinks,
+    int32_t batch, int32_t q_len, int32_t max_kv_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    float softmax_scale, int32_t causal, int32_t window, int32_t kv_chunk,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of workspace attn_sink_decode_paged needs for these host scalars (0 if they are
  * invalid). Monotone non-decreasing in batch, q_len, max_kv_len and num_q_heads.
  */

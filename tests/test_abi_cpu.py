@@ -134,6 +134,29 @@ def test_decode_argument_errors(amd):
     assert _decode(amd, batch=0, q=None, ws=None) == OK
 
 
+def _decode_partials(amd, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, max_pages=512, num_pages=100, kv_lens=FAKE, sinks=None, batch=4,
+             q_len=1, max_kv=8192, hq=64, hkv=8, d=64, page=16, scale=0.125, causal=1, window=0, chunk=512,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return amd.lib.attn_sink_decode_paged_partials(a["q"], a["k"], a["v"], a["table"], a["max_pages"],
+                                                   a["num_pages"], a["kv_lens"], a["sinks"], a["batch"], a["q_len"],
+                                                   a["max_kv"], a["hq"], a["hkv"], a["d"], a["page"], a["scale"],
+                                                   a["causal"], a["window"], a["chunk"], a["ws"], a["ws_bytes"],
+                                                   a["stream"])
+
+
+def test_decode_partials_argument_errors(amd):
+    """The split-only entry point validates exactly like attn_sink_decode_paged (it has no out)."""
+    for kw, want in [(dict(d=128), UNSUPPORTED), (dict(q_len=9), UNSUPPORTED), (dict(q_len=0), INVALID),
+                     (dict(page=24), UNSUPPORTED), (dict(chunk=100), UNSUPPORTED), (dict(hq=60, hkv=8), INVALID),
+                     (dict(scale=float("nan")), INVALID), (dict(q=None), INVALID), (dict(ws=None), INVALID),
+                     (dict(ws=FAKE + 16), INVALID), (dict(ws_bytes=0), WS_SMALL),
+                     (dict(batch=0, q=None, ws=None), OK)]:
+        assert _decode_partials(amd, **kw) == want, kw
+        assert _decode(amd, **kw) == want, kw
+
+
 def test_merge_argument_errors(amd):
     f = amd.lib.attn_sink_merge_partials
     assert f(FAKE, FAKE, 10, FAKE, 4, 8, 128, FAKE, None, None) == UNSUPPORTED

@@ -274,6 +274,30 @@ def test_decode_plan_is_bit_exact_and_partials_match(amd):
     assert_close(o_p.astype(np.float64), l_p.astype(np.float64), ro_p, rl_p, "partials")
 
 
+def test_decode_partials_then_merge_equals_decode(amd):
+    """The split-only entry point followed by attn_sink_merge_partials reproduces attn_sink_decode_paged
+    bit for bit (the same kernels run), and its plan and partials match the oracle's."""
+    spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=5, q_len=3, kv_len=(1, 1700), hq=16, hkv=2, seed=71)
+    inp = make_paged(spec)
+    d = dev_paged(inp)
+    out, lse = run_decode(amd, d, inp, spec)
+    parts = amd.attn_sink_decode_paged_partials(d["q"], d["k"], d["v"], d["table"], d["lens"], d["sinks"],
+                                                spec.q_len, inp["max_kv_len"], spec.scale, spec.causal, spec.window,
+                                                spec.kv_chunk)
+    out2, lse2 = amd.attn_sink_merge_partials(parts["o_partial"], parts["lse_partial"], parts["partial_indptr"])
+    torch.cuda.synchronize()
+    assert np.array_equal(out_f64(out2), out) and np.array_equal(lse2.cpu().numpy().astype(np.float64), lse)
+    exp_counts, exp_indptr = oracle.plan_chunks(inp["kv_lens"], spec.q_len, spec.kv_chunk)
+    assert parts["chunk_counts"].cpu().numpy().tolist() == exp_counts
+    assert parts["partial_indptr"].cpu().numpy().tolist() == exp_indptr
+    n = exp_indptr[-1]
+    ro_p, rl_p, _, _ = oracle.split_decode(f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"]),
+                                           inp["page_table"], inp["kv_lens"], inp["sinks"], spec.q_len, spec.scale,
+                                           spec.kv_chunk)
+    assert_close(parts["o_partial"][:n].cpu().numpy().astype(np.float64),
+                 parts["lse_partial"][:n].cpu().numpy().astype(np.float64), ro_p, rl_p, "partials entry point")
+
+
 def test_merge_kernel_on_oracle_partials(amd):
     spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=4, kv_len=(1, 1600), hq=8, hkv=2, seed=64)
     inp = make_paged(spec, kv_lens=[1600, 2, 700, 0])
