@@ -148,6 +148,25 @@ __device__ __forceinline__ void buffer_load16_lds_async_nt(__amdgpu_buffer_rsrc_
 
 // Workgroup barrier that is also a compiler barrier for memory accesses, without the
 // s_waitcnt vmcnt(0) / lgkmcnt(0) that __syncthreads() adds.
+// 16-byte buffer load (at byte offset voff + OFF of r) that the compiler does not track: the
+// caller retires it with an explicit s_waitcnt vmcnt and calls tie() on the value before use.
+template <int OFF>
+__device__ __forceinline__ u32x4 buffer_load16_untracked(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  u32x4 v;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3" : "=v"(v) : "v"(voff), "s"(r), "i"(OFF) : "memory");
+  return v;
+}
+// Marks v as written here, so that no use of v moves above this point.
+__device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// Lane index that the compiler can neither hoist nor keep alive across a loop: per-lane
+// addresses derived from it are recomputed where they are used.
+__device__ __forceinline__ int opaque_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // s_waitcnt vmcnt(n) (n < 16), leaving the other counters alone.

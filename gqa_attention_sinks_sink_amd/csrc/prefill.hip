@@ -362,6 +362,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int TOK = ROWS / GP;
   constexpr int kRing = 4;
   __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[kRing][kStageBytes];
+  // Per-wave staging of the output rows (64 rows x 128 bytes per wave).
+  __shared__ __attribute__((aligned(16))) unsigned char out_lds[NW][64 * kHeadDim * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -396,6 +398,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const size_t seq_base = (size_t)k0 * p.hkv * kHeadDim;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + seq_base, (uint32_t)Lk * row_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + seq_base, (uint32_t)Lk * row_bytes);
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc_uniform(p.q + (size_t)q0 * p.hq * kHeadDim, (uint32_t)Lq * p.hq * (kHeadDim * 2));
+
+  // A lane's head is head0 + lane % GP in every row block and pass (GP divides 32). The GP
+  // sink logits come in through scalar loads, once per workgroup.
+  float sink_l2 = kNegInf;
+  if (p.sinks != nullptr) {
+    float sv[GP];
+#pragma unroll
+    for (int i = 0; i < GP; ++i) sv[i] = p.sinks[head0 + i];
+    sink_l2 = sv[0];
+#pragma unroll
+    for (int i = 1; i < GP; ++i) sink_l2 = ((lane & (GP - 1)) == i) ? sv[i] : sink_l2;
+    sink_l2 *= kLog2e;
+  }
 
   for (int pass = 0; pass < (p.pair_blocks ? 2 : 1); ++pass) {
   if (pass == 0 && unit >= (p.pair_blocks ? (n_blk + 1) / 2 : n_blk)) break;
@@ -410,7 +427,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     vl = 0;
     if (vh < vl) vh = vl;
   };
+  // Q rows of the pass. Rows past the end load the last valid row (their results are never
+  // stored). The loads are untracked, so that waiting for them does not also wait for the K/V
+  // tiles issued after them; they have landed once the first tile has, where qb is tied.
   u32x4 qb[RB][4];
+  {
+    const int ln = opaque_lane_id();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = (w * RB + rb) * 32 + (ln & 31);
+      const int t = min(ts + r / GP, te - 1);
+      const uint32_t voff = ((uint32_t)t * p.hq + head0 + (r % GP)) * (kHeadDim * 2) + (ln >> 5) * 16;
+      qb[rb][0] = buffer_load16_untracked<0>(rq, voff);
+      qb[rb][1] = buffer_load16_untracked<32>(rq, voff);
+      qb[rb][2] = buffer_load16_untracked<64>(rq, voff);
+      qb[rb][3] = buffer_load16_untracked<96>(rq, voff);
+    }
+  }
+  auto tie_q = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) tie(qb[rb][ks]);
+  };
   float m[RB], lsum[RB];
   f32x16 o[RB][2];
   int hi_min = 0x7fffffff, lo_max = -0x7fffffff;
@@ -418,14 +457,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int rb = 0; rb < RB; ++rb) {
     const int r = (w * RB + rb) * 32 + r32;
     const int t = ts + r / GP;
-    const int head = head0 + (r % GP);
     const bool row_ok = t < te;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      qb[rb][ks] = row_ok ? *reinterpret_cast<const u32x4*>(p.q + ((size_t)(q0 + t) * p.hq + head) * kHeadDim + ks * 16 + half * 8)
-                          : u32x4{0, 0, 0, 0};
-    }
-    m[rb] = (p.sinks != nullptr) ? p.sinks[head] * kLog2e : kNegInf;
+    m[rb] = sink_l2;
     lsum[rb] = (half == 0) ? 1.0f : 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) { o[rb][0][i] = 0.f; o[rb][1][i] = 0.f; }
@@ -452,13 +485,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (nt > 0) {
     // Wave w loads rows [8w, 8w + 8) of a tile's K and V (one 1 KB load each); lane i writes
     // chunk position i & 7 of row i >> 3, with the same swizzles as the 4-wave kernel.
+    // The per-lane part of the offsets is rebuilt from the lane id at every issue: kept in
+    // registers across the pass, it would be spilled, and each reload would wait for every
+    // tile in flight.
     auto issue_tile = [&](int t) {
-      const int r = 8 * w + (lane >> 3);
-      const int pch = lane & 7;
-      const uint32_t rowoff = (uint32_t)(jb + t * kTileN + r) * row_bytes + (uint32_t)kvh * (kHeadDim * 2);
+      const int ln = opaque_lane_id();
+      const int r8 = ln >> 3;  // row 8 w + r8 of the tile
+      const int pch = ln & 7;
+      const uint32_t row0 = (uint32_t)(jb + t * kTileN + 8 * w) * row_bytes + (uint32_t)kvh * (kHeadDim * 2);
+      const uint32_t rowoff = (uint32_t)r8 * row_bytes + row0;
+      // (r >> 1) & 7 and ((r >> 1) & 1) * 4 for r = 8 w + r8.
+      const int swz_k = (r8 >> 1) | ((w & 1) << 2);
+      const int swz_v = (r8 & 2) << 1;
       unsigned char* dst = kv_lds[t & (kRing - 1)] + 8 * w * 128;
-      buffer_load16_lds_async(rk, dst, rowoff + (uint32_t)((pch ^ ((r >> 1) & 7)) * 16));
-      buffer_load16_lds_async(rv, dst + kTileBytes, rowoff + (uint32_t)((pch ^ (((r >> 1) & 1) * 4)) * 16));
+      buffer_load16_lds_async(rk, dst, rowoff + (uint32_t)((pch ^ swz_k) << 4));
+      buffer_load16_lds_async(rv, dst + kTileBytes, rowoff + (uint32_t)((pch ^ swz_v) << 4));
     };
     issue_tile(0);
     if (nt > 1) issue_tile(1);
@@ -632,6 +673,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const std::false_type no{};
     if (lag) sync_slot(0);
     sync_slot(lag);
+    tie_q();
     prio_matrix();
     matrix_phase(0, no, yes);
     sync_slot(1 + lag);
@@ -654,32 +696,52 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // The last loads were retired in the loop; every wave is done with the ring before the
     // next pass reuses it.
     __syncthreads();
+  } else {
+    // No key is visible: Q is not needed, but its registers must not be reused before the
+    // loads have landed.
+    WAIT_VMCNT(0);
+    tie_q();
   }
 
+  // O goes through this wave's LDS slice: the accumulator layout gives a lane 8-byte pieces
+  // of one row, the stores then write whole 128-byte rows (8 lanes per row, 8 rows per
+  // instruction). 16-byte chunk c of row i sits at chunk position c ^ (i & 7).
+  {
+    const int ln = opaque_lane_id();
+    const int hf = ln >> 5;
+    unsigned char* ow = out_lds[w];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float lt = lsum[rb] + shfl_xor(lsum[rb], 32);
-    const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
-    const int r = (w * RB + rb) * 32 + r32;
-    const int t = ts + r / GP;
-    const int head = head0 + (r % GP);
-    if (t < te) {
-      uint16_t* orow = p.out + ((size_t)(q0 + t) * p.hq + head) * kHeadDim;
+    for (int rb = 0; rb < RB; ++rb) {
+      const float lt = lsum[rb] + shfl_xor(lsum[rb], 32);
+      const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
+      const int i = rb * 32 + (ln & 31);
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = dt * 32 + 8 * q4 + 4 * half;
           u32x2 pkd;
           pkd[0] = pack_bf16x2(o[rb][dt][q4 * 4 + 0] * inv, o[rb][dt][q4 * 4 + 1] * inv);
           pkd[1] = pack_bf16x2(o[rb][dt][q4 * 4 + 2] * inv, o[rb][dt][q4 * 4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d0) = pkd;
+          const int c = dt * 4 + q4;
+          *reinterpret_cast<u32x2*>(ow + i * 128 + ((c ^ (i & 7)) << 4) + hf * 8) = pkd;
         }
       }
-      if (p.lse != nullptr && half == 0) {
-        p.lse[(size_t)(q0 + t) * p.hq + head] =
+      const int r = (w * RB + rb) * 32 + (ln & 31);
+      const int t = ts + r / GP;
+      if (p.lse != nullptr && hf == 0 && t < te) {
+        p.lse[(size_t)(q0 + t) * p.hq + head0 + (r % GP)] =
             (m[rb] == kNegInf || !(lt > 0.f)) ? kNegInf : (m[rb] + fast_log2(lt)) * kLn2;
       }
+    }
+    const int c = ln & 7;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = 8 * k + (ln >> 3);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ow + i * 128 + ((c ^ (i & 7)) << 4));
+      const int r = (w * RB + (i >> 5)) * 32 + (i & 31);
+      const int t = ts + r / GP;
+      if (t < te)
+        *reinterpret_cast<u32x4*>(p.out + ((size_t)(q0 + t) * p.hq + head0 + (r % GP)) * kHeadDim + c * 8) = v;
     }
   }
   }  // pass
@@ -737,8 +799,10 @@ int prefill_row_blocks(int max_q, int gp) {
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (p.batch == 0 || p.total_q == 0 || p.max_q == 0) return hipSuccess;
   const int gp = prefill_heads_per_tile(p.group);
-  // long sequences without a window: the 8-wave ping-pong kernel
-  if (p.window == 0 && p.max_q >= 2048) return launch_pp(p, gp, stream);
+  // Long sequences without a window: the 8-wave ping-pong kernel (which addresses a
+  // sequence's Q rows with 32-bit byte offsets).
+  if (p.window == 0 && p.max_q >= 2048 && (int64_t)p.max_q * p.hq * (kHeadDim * 2) <= INT32_MAX)
+    return launch_pp(p, gp, stream);
   return prefill_row_blocks(p.max_q, gp) == 2 ? launch_rb<2>(p, gp, stream) : launch_rb<1>(p, gp, stream);
 }
 
