@@ -92,9 +92,10 @@ attn_sink_status attn_sink_prefill(const void* q, const void* k, const void* v, 
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
   if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr) return ATTN_SINK_ERR_INVALID_ARG;
   if (total_kv > 0 && (k == nullptr || v == nullptr)) return ATTN_SINK_ERR_INVALID_ARG;
-  // K/V of one sequence are addressed with 32-bit byte offsets.
+  // Q, K and V of one sequence are addressed with 32-bit byte offsets.
   if ((int64_t)max_seqlen_kv * num_kv_heads * kSupportedHeadDim * 2 + 64ll * num_kv_heads * kSupportedHeadDim * 2 > INT32_MAX)
     return ATTN_SINK_ERR_UNSUPPORTED;
+  if ((int64_t)max_seqlen_q * num_q_heads * kSupportedHeadDim * 2 > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t gp = prefill_heads_per_tile(group);
   const int64_t tok = 128 * prefill_row_blocks(max_seqlen_q, gp) / gp;  // query tokens per workgroup

@@ -54,10 +54,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // (16 lanes, 16 rows, one chunk) and the 8 B transposing V reads (32 lanes, 4 rows,
   // 64 B each) hit 64 distinct banks.
   __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[kStages][kStageBytes];
+  // Per-wave staging of the output rows (32 RB rows x 128 bytes per wave).
+  __shared__ __attribute__((aligned(16))) unsigned char out_lds[kThreads / 64][32 * RB * kHeadDim * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;  // which 32-lane half
   const int r32 = lane & 31;
 
@@ -87,6 +89,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float c = p.scale_log2;
   const int n_blk = (Lq + TOK - 1) / TOK;
 
+  const uint32_t row_bytes = (uint32_t)p.hkv * (kHeadDim * 2);  // one token of K (or V), all heads
+  const size_t seq_base = (size_t)k0 * p.hkv * kHeadDim;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc_uniform(p.k + seq_base, (uint32_t)Lk * row_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc_uniform(p.v + seq_base, (uint32_t)Lk * row_bytes);
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc_uniform(p.q + (size_t)q0 * p.hq * kHeadDim, (uint32_t)Lq * p.hq * (kHeadDim * 2));
+
+  // A lane's head is head0 + lane % GP in every row block and pass (GP divides 32). The GP
+  // sink logits come in through scalar loads, once per workgroup.
+  float sink_l2 = kNegInf;
+  if (p.sinks != nullptr) {
+    float sv[GP];
+#pragma unroll
+    for (int i = 0; i < GP; ++i) sv[i] = p.sinks[head0 + i];
+    sink_l2 = sv[0];
+#pragma unroll
+    for (int i = 1; i < GP; ++i) sink_l2 = ((lane & (GP - 1)) == i) ? sv[i] : sink_l2;
+    sink_l2 *= kLog2e;
+  }
+
   // A unit is one row block, or with causal pairing the blocks u and n_blk - 1 - u, whose
   // key ranges add up to about the same length for every unit.
   for (int pass = 0; pass < (p.pair_blocks ? 2 : 1); ++pass) {
@@ -104,7 +126,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     vl = (p.window > 0) ? max(0, pos - p.window + 1) : 0;
     if (vh < vl) vh = vl;
   };
-  u32x4 qb[RB][4];  // Q^T as the B operand: column = row, k = head dim (16 per step)
+  // Q^T as the B operand: column = row, k = head dim (16 per step). Rows past the end load
+  // the last valid row (their results are never stored). The loads are untracked, so that
+  // waiting for them does not also wait for the K/V tiles issued after them; qb is tied
+  // after each tile wait, which covers them.
+  u32x4 qb[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = (w * RB + rb) * 32 + r32;
+    const int t = min(ts + r / GP, te - 1);
+    const uint32_t voff = ((uint32_t)t * p.hq + head0 + (r % GP)) * (kHeadDim * 2) + half * 16;
+    qb[rb][0] = buffer_load16_untracked<0>(rq, voff);
+    qb[rb][1] = buffer_load16_untracked<32>(rq, voff);
+    qb[rb][2] = buffer_load16_untracked<64>(rq, voff);
+    qb[rb][3] = buffer_load16_untracked<96>(rq, voff);
+  }
+  auto tie_q = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) tie(qb[rb][ks]);
+  };
   float m[RB], lsum[RB];
   f32x16 o[RB][2];
   int hi_min = 0x7fffffff, lo_max = -0x7fffffff, hi_max = -0x7fffffff, lo_min = 0x7fffffff;
@@ -112,15 +154,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int rb = 0; rb < RB; ++rb) {
     const int r = (w * RB + rb) * 32 + r32;
     const int t = ts + r / GP;
-    const int head = head0 + (r % GP);
     const bool row_ok = t < te;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      qb[rb][ks] = row_ok ? *reinterpret_cast<const u32x4*>(p.q + ((size_t)(q0 + t) * p.hq + head) * kHeadDim + ks * 16 + half * 8)
-                          : u32x4{0, 0, 0, 0};
-    }
     // Online softmax state; the sink seeds the running max, d starts at 1 (held by lane half 0).
-    m[rb] = (p.sinks != nullptr) ? p.sinks[head] * kLog2e : kNegInf;
+    m[rb] = sink_l2;
     lsum[rb] = (half == 0) ? 1.0f : 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) { o[rb][0][i] = 0.f; o[rb][1][i] = 0.f; }
@@ -158,11 +194,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // K/V tiles: buffer loads bounded by the sequence's last key return zeros past it (exact
   // zeros for keys that are masked anyway). Wave w fills rows [16w, 16w + 16) of a tile's K
-  // and V with two 1 KB loads each; lane i writes chunk position i & 7 of row i >> 3.
-  const uint32_t row_bytes = (uint32_t)p.hkv * (kHeadDim * 2);  // one token of K (or V), all heads
-  const size_t seq_base = (size_t)k0 * p.hkv * kHeadDim;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + seq_base, (uint32_t)Lk * row_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + seq_base, (uint32_t)Lk * row_bytes);
+  // and V with two 1 KB loads each; lane i writes chunk position i & 7 of row i >> 3. The
+  // loads are hidden from the compiler (its own tracking would wait for all of them before
+  // any LDS read); the waits below retire them explicitly.
   auto issue_tile = [&](int jt, int st) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
@@ -170,8 +204,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int pch = lane & 7;
       const uint32_t rowoff = (uint32_t)(jt + r) * row_bytes + (uint32_t)kvh * (kHeadDim * 2);
       unsigned char* dst = kv_lds[st] + (16 * w + 8 * ii) * 128;
-      buffer_load16_lds(rk, dst, rowoff + (uint32_t)((pch ^ ((r >> 1) & 7)) * 16));
-      buffer_load16_lds(rv, dst + kTileBytes, rowoff + (uint32_t)((pch ^ (((r >> 1) & 1) * 4)) * 16));
+      buffer_load16_lds_async(rk, dst, rowoff + (uint32_t)((pch ^ ((r >> 1) & 7)) * 16));
+      buffer_load16_lds_async(rv, dst + kTileBytes, rowoff + (uint32_t)((pch ^ (((r >> 1) & 1) * 4)) * 16));
     }
   };
 
@@ -190,7 +224,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     } else {
       WAIT_VMCNT(0);
     }
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
+    tie_q();
     if (jt + 2 * kTileN < je) issue_tile(jt + 2 * kTileN, st == 0 ? 2 : st - 1);
     const unsigned char* kt_lds = kv_lds[st];
     const unsigned char* vt_lds = kv_lds[st] + kTileBytes;
@@ -311,33 +346,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Retire the loads past the last tile and let every wave finish with the ring before it
   // is reused.
   WAIT_VMCNT(0);
+  tie_q();
   __syncthreads();
 
-  // Epilogue: out = O / d, lse = m + log2(d) converted to natural log.
+  // Epilogue: out = O / d, lse = m + log2(d) converted to natural log. O goes through this
+  // wave's LDS slice: the accumulator layout gives a lane 8-byte pieces of one row, the
+  // stores then write whole 128-byte rows (8 lanes per row). 16-byte chunk c of row i sits
+  // at chunk position c ^ (i & 7).
+  {
+    // (Addresses from a fresh lane id: the compiler would otherwise compute them before the
+    // key loop and keep them in spill slots.)
+    const int ln = opaque_lane_id();
+    const int hf = ln >> 5;
+    unsigned char* ow = out_lds[w];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float lt = lsum[rb] + shfl_xor(lsum[rb], 32);
-    const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
-    const int r = (w * RB + rb) * 32 + r32;
-    const int t = ts + r / GP;
-    const int head = head0 + (r % GP);
-    if (t < te) {
-      uint16_t* orow = p.out + ((size_t)(q0 + t) * p.hq + head) * kHeadDim;
+    for (int rb = 0; rb < RB; ++rb) {
+      const float lt = lsum[rb] + shfl_xor(lsum[rb], 32);
+      const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
+      const int i = rb * 32 + (ln & 31);
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = dt * 32 + 8 * q4 + 4 * half;
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[rb][dt][q4 * 4 + 0] * inv, o[rb][dt][q4 * 4 + 1] * inv);
-          pk[1] = pack_bf16x2(o[rb][dt][q4 * 4 + 2] * inv, o[rb][dt][q4 * 4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d0) = pk;
+          u32x2 pkd;
+          pkd[0] = pack_bf16x2(o[rb][dt][q4 * 4 + 0] * inv, o[rb][dt][q4 * 4 + 1] * inv);
+          pkd[1] = pack_bf16x2(o[rb][dt][q4 * 4 + 2] * inv, o[rb][dt][q4 * 4 + 3] * inv);
+          const int cc = dt * 4 + q4;
+          *reinterpret_cast<u32x2*>(ow + i * 128 + ((cc ^ (i & 7)) << 4) + hf * 8) = pkd;
         }
       }
-      if (p.lse != nullptr && half == 0) {
-        p.lse[(size_t)(q0 + t) * p.hq + head] =
+      const int r = (w * RB + rb) * 32 + (ln & 31);
+      const int t = ts + r / GP;
+      if (p.lse != nullptr && hf == 0 && t < te) {
+        p.lse[(size_t)(q0 + t) * p.hq + head0 + (r % GP)] =
             (m[rb] == kNegInf || !(lt > 0.f)) ? kNegInf : (m[rb] + fast_log2(lt)) * kLn2;
       }
+    }
+    const int cc = ln & 7;
+#pragma unroll
+    for (int k = 0; k < 4 * RB; ++k) {
+      const int i = 8 * k + (ln >> 3);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ow + i * 128 + ((cc ^ (i & 7)) << 4));
+      const int r = (w * RB + (i >> 5)) * 32 + (i & 31);
+      const int t = ts + r / GP;
+      if (t < te)
+        *reinterpret_cast<u32x4*>(p.out + ((size_t)(q0 + t) * p.hq + head0 + (r % GP)) * kHeadDim + cc * 8) = v;
     }
   }
   }  // pass
@@ -799,10 +852,8 @@ int prefill_row_blocks(int max_q, int gp) {
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (p.batch == 0 || p.total_q == 0 || p.max_q == 0) return hipSuccess;
   const int gp = prefill_heads_per_tile(p.group);
-  // Long sequences without a window: the 8-wave ping-pong kernel (which addresses a
-  // sequence's Q rows with 32-bit byte offsets).
-  if (p.window == 0 && p.max_q >= 2048 && (int64_t)p.max_q * p.hq * (kHeadDim * 2) <= INT32_MAX)
-    return launch_pp(p, gp, stream);
+  // Long sequences without a window: the 8-wave ping-pong kernel.
+  if (p.window == 0 && p.max_q >= 2048) return launch_pp(p, gp, stream);
   return prefill_row_blocks(p.max_q, gp) == 2 ? launch_rb<2>(p, gp, stream) : launch_rb<1>(p, gp, stream);
 }
 

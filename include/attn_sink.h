@@ -84,7 +84,9 @@ typedef enum {
  *   lse          fp32 [total_q, num_q_heads] or NULL.
  * Constraints: batch >= 0, num_q_heads % num_kv_heads == 0, head_dim == 64,
  * softmax_scale finite and > 0; q, k, v, out and the cu_seqlens pointers non-NULL when
- * batch > 0 and total_q > 0.
+ * batch > 0 and total_q > 0. One sequence's Q rows (max_seqlen_q * num_q_heads * 128
+ * bytes) and K or V rows (plus one 64-key tile) must each span less than 2^31 bytes,
+ * else ATTN_SINK_ERR_UNSUPPORTED.
  */
 attn_sink_status attn_sink_prefill(
     const void* q, const void* k, const void* v, const float* sinks,

@@ -92,6 +92,9 @@ def test_prefill_argument_errors(amd):
     assert _prefill(amd, out=None) == INVALID
     assert _prefill(amd, cu_q=None) == INVALID
     assert _prefill(amd, k=None) == INVALID
+    # one sequence's rows must span less than 2^31 bytes (32-bit offsets in the kernels)
+    assert _prefill(amd, max_q=1 << 18, hq=64, hkv=8) == UNSUPPORTED
+    assert _prefill(amd, max_kv=1 << 21, hq=8, hkv=8) == UNSUPPORTED
     # nothing to do: accepted without launching anything
     assert _prefill(amd, batch=0, q=None, out=None) == OK
     assert _prefill(amd, total_q=0, q=None, out=None) == OK
