@@ -54,8 +54,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // (16 lanes, 16 rows, one chunk) and the 8 B transposing V reads (32 lanes, 4 rows,
   // 64 B each) hit 64 distinct banks.
   __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[kStages][kStageBytes];
-  // Per-wave staging of the output rows (32 RB rows x 128 bytes per wave).
-  __shared__ __attribute__((aligned(16))) unsigned char out_lds[kThreads / 64][32 * RB * kHeadDim * 2];
+  // Per-wave staging of the output rows (32 RB rows x 128 bytes per wave). With RB = 1 it
+  // fits the last ring stage, which no wave writes again before the next pass's first
+  // barrier; that keeps the LDS of three workgroups within one CU.
+  __shared__ __attribute__((aligned(16))) unsigned char out_lds[kThreads / 64][RB == 1 ? 16 : 32 * RB * kHeadDim * 2];
+  static_assert(kStageBytes >= (kThreads / 64) * 32 * kHeadDim * 2, "RB = 1 staging fits one ring stage");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -358,7 +361,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // key loop and keep them in spill slots.)
     const int ln = opaque_lane_id();
     const int hf = ln >> 5;
-    unsigned char* ow = out_lds[w];
+    unsigned char* ow;
+    if constexpr (RB == 1) {
+      ow = kv_lds[kStages - 1] + w * (32 * kHeadDim * 2);
+    } else {
+      ow = out_lds[w];
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float lt = lsum[rb] + shfl_xor(lsum[rb], 32);
