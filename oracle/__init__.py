@@ -21,6 +21,6 @@ returned log-sum-exp includes the sink term; here it does (parity unpinned by th
 pages: a stated reading).
 """
 from .attention import (  # noqa: F401
-    attend, attention_weights, prefill_varlen, gather_pages, decode_paged,
+    attend, attention_weights, prefill_varlen, gather_pages, decode_paged, prefill_paged,
     online_partials, split_decode, merge, plan_chunks,
 )

@@ -164,6 +164,30 @@ def decode_paged(q, k_cache, v_cache, page_table, kv_lens, sinks, q_len, scale, 
     return out, lse
 
 
+def prefill_paged(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, sinks, scale, causal, window=0,
+                  seqs: Optional[Sequence[int]] = None, rows: Optional[dict] = None):
+    """Chunked prefill against a paged cache ("Fast Embeddings on GPUs": the LLM path runs
+    prefill as well as decode on paged KV). Sequence b owns Q rows cu_q[b]:cu_q[b+1], the
+    last Lq_b = cu_q[b+1] - cu_q[b] of its kv_lens[b] tokens, so query token t sits at
+    position kv_lens[b] - Lq_b + t; its K/V come through page_table[b]. ``seqs`` limits the
+    sequences computed, ``rows[b]`` (optional) the query tokens of sequence b (local
+    indices). Uncomputed rows are NaN.
+    """
+    cu_q = np.asarray(cu_seqlens_q, dtype=np.int64)
+    total_q, hq, d = q.shape
+    out = np.full((total_q, hq, d), np.nan)
+    lse = np.full((total_q, hq), np.nan)
+    for b in (range(len(kv_lens)) if seqs is None else seqs):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        L = int(kv_lens[b])
+        kb = gather_pages(k_cache, page_table[b], L).astype(np.float64)
+        vb = gather_pages(v_cache, page_table[b], L).astype(np.float64)
+        qb = np.asarray(q[q0:q1], dtype=np.float64)
+        sel = np.arange(q1 - q0) if rows is None or b not in rows else np.asarray(rows[b], dtype=np.int64)
+        o, l = attend(qb[sel], kb, vb, sinks, scale, causal, window, q_pos=_positions(q1 - q0, L)[sel])
+        out[q0 + sel], lse[q0 + sel] = o, l
+    return out, lse
+
 # ----------------------------------------------------------------------------------
 # Streaming form, as the "Attention sinks" section describes it
 # ----------------------------------------------------------------------------------

@@ -16,7 +16,7 @@ import torch
 import mpmath
 
 import oracle
-from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_varlen, scaled
+from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_paged_prefill, make_varlen, scaled
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_derived.json")
 
@@ -268,6 +268,82 @@ def test_paged_equals_contiguous_and_permutation_invariant():
                                      spec.scale, True, 0)
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
 
+
+# ---------------------------------------------------------------------------------------
+# c-P8b: chunked prefill on a paged cache, pinned by routes that do not use its gather
+# ---------------------------------------------------------------------------------------
+def _flat_gather(cache, table_row, L):
+    """Contiguous [L, hkv, d] copy through a flat token index (not oracle.gather_pages)."""
+    tok = np.arange(L)
+    P = cache.shape[2]
+    return cache[table_row[tok // P], :, tok % P, :]
+
+
+def _f64(x):
+    return bf16_bits_to_f32(x).astype(np.float64)
+
+
+def test_paged_prefill_without_context_equals_varlen():
+    spec = scaled(CONFIGS["chunked_prefill"], batch=3, q_len=(17, 70), ctx_len=(0, 0), hq=8, hkv=2, seed=21)
+    inp = make_paged_prefill(spec)
+    q, kc, vc = _f64(inp["q"]), _f64(inp["k_cache"]), _f64(inp["v_cache"])
+    cu = inp["cu_seqlens_q"]
+    k = np.concatenate([_flat_gather(kc, inp["page_table"][b], L) for b, L in enumerate(inp["kv_lens"])])
+    v = np.concatenate([_flat_gather(vc, inp["page_table"][b], L) for b, L in enumerate(inp["kv_lens"])])
+    for causal, window in [(True, 0), (True, 9), (False, 0)]:
+        a = oracle.prefill_paged(q, kc, vc, inp["page_table"], cu, inp["kv_lens"], inp["sinks"], spec.scale,
+                                 causal, window)
+        b = oracle.prefill_varlen(q, k, v, cu, cu, inp["sinks"], spec.scale, causal, window)
+        np.testing.assert_allclose(a[0], b[0], atol=1e-13, rtol=0)
+        np.testing.assert_allclose(a[1], b[1], atol=1e-13, rtol=0)
+
+
+def test_paged_prefill_chunk_is_the_tail_of_a_full_prefill():
+    # The chunk's rows are the last rows of a causal prefill over context + chunk: that pins
+    # the alignment of the queries to the newest positions.
+    spec = scaled(CONFIGS["chunked_prefill"], batch=2, q_len=(5, 40), ctx_len=(3, 60), hq=4, hkv=1, seed=22)
+    inp = make_paged_prefill(spec)
+    q, kc, vc = _f64(inp["q"]), _f64(inp["k_cache"]), _f64(inp["v_cache"])
+    rng = np.random.default_rng(3)
+    for window in (0, 7):
+        out, lse = oracle.prefill_paged(q, kc, vc, inp["page_table"], inp["cu_seqlens_q"], inp["kv_lens"],
+                                        inp["sinks"], spec.scale, True, window)
+        for b, L in enumerate(inp["kv_lens"]):
+            q0, q1 = int(inp["cu_seqlens_q"][b]), int(inp["cu_seqlens_q"][b + 1])
+            ctx_q = rng.standard_normal((L - (q1 - q0), spec.hq, 64))
+            full_q = np.concatenate([ctx_q, q[q0:q1]])
+            k, v = _flat_gather(kc, inp["page_table"][b], L), _flat_gather(vc, inp["page_table"][b], L)
+            fo, fl = _sdpa_plain(full_q, k, v, spec.scale, True, window)
+            sig = 1.0 / (1.0 + np.exp(inp["sinks"][None, :].astype(np.float64) - fl))
+            np.testing.assert_allclose(out[q0:q1], (fo * sig[..., None])[L - (q1 - q0):], atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[q0:q1], np.logaddexp(fl, inp["sinks"][None, :])[L - (q1 - q0):],
+                                       atol=1e-12, rtol=0)
+
+
+def test_paged_prefill_brute_force_50_digits():
+    spec = scaled(CONFIGS["chunked_prefill"], batch=2, q_len=(2, 3), ctx_len=(1, 4), hq=2, hkv=1, page_size=2,
+                  seed=23)
+    inp = make_paged_prefill(spec)
+    q, kc, vc = _f64(inp["q"])[..., :8], _f64(inp["k_cache"])[..., :8], _f64(inp["v_cache"])[..., :8]
+    out, lse = oracle.prefill_paged(q, kc, vc, inp["page_table"], inp["cu_seqlens_q"], inp["kv_lens"],
+                                    inp["sinks"], 0.35, True, 0)
+    for b, L in enumerate(inp["kv_lens"]):
+        q0, q1 = int(inp["cu_seqlens_q"][b]), int(inp["cu_seqlens_q"][b + 1])
+        bo, bl = _brute(q[q0:q1], _flat_gather(kc, inp["page_table"][b], L), _flat_gather(vc, inp["page_table"][b], L),
+                        inp["sinks"], 0.35, True, 0)
+        np.testing.assert_allclose(out[q0:q1], bo, atol=1e-13, rtol=0)
+        np.testing.assert_allclose(lse[q0:q1], bl, atol=1e-13, rtol=0)
+
+
+def test_paged_prefill_uniform_chunks_equal_decode_paged():
+    spec = scaled(CONFIGS["chunked_prefill"], batch=3, q_len=(5, 5), ctx_len=(10, 50), hq=8, hkv=2, seed=24)
+    inp = make_paged_prefill(spec)
+    q, kc, vc = _f64(inp["q"]), _f64(inp["k_cache"]), _f64(inp["v_cache"])
+    a = oracle.prefill_paged(q, kc, vc, inp["page_table"], inp["cu_seqlens_q"], inp["kv_lens"], inp["sinks"],
+                             spec.scale, True, 0)
+    b = oracle.decode_paged(q, kc, vc, inp["page_table"], inp["kv_lens"], inp["sinks"], 5, spec.scale, True, 0)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-13, rtol=0)
 
 # ---------------------------------------------------------------------------------------
 # c-P9: a large sink takes the weight

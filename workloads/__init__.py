@@ -12,7 +12,7 @@ multi-token verification of "Accelerating Sonar through speculation" (MTP sectio
 
 Recipe (fixed, documented in the design notes):
   * ``numpy.random.default_rng(seed)``; draw order: lengths -> page permutation ->
-    Q -> K -> V -> sinks.
+    Q -> K -> V -> sinks (chunked prefill draws chunk lengths, then cached lengths).
   * Q/K/V are fp32 N(0, 1) rounded to bf16 with round-to-nearest-even.
   * Sinks are fp32 ``sink_std * N(0, 1)``; ``sink_std=None`` means the sink is
     disabled (-inf for every head).
@@ -31,8 +31,8 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = [
-    "VarlenSpec", "PagedSpec", "CONFIGS", "bf16_round_bits", "bf16_bits_to_f32",
-    "make_varlen", "make_paged", "scaled",
+    "VarlenSpec", "PagedSpec", "PagedPrefillSpec", "CONFIGS", "bf16_round_bits", "bf16_bits_to_f32",
+    "make_varlen", "make_paged", "make_paged_prefill", "scaled",
 ]
 
 
@@ -109,6 +109,28 @@ class PagedSpec:
         return 1.0 / float(np.sqrt(self.head_dim))
 
 
+@dataclass(frozen=True)
+class PagedPrefillSpec:
+    """Chunked prefill against a paged KV cache: every sequence appends a chunk of new tokens
+    (its queries) to a cache that already holds ctx_len tokens; kv_len = ctx_len + q_len."""
+    name: str
+    batch: int
+    q_len: Tuple[int, int]           # inclusive uniform range of the chunk length
+    ctx_len: Tuple[int, int]         # inclusive uniform range of the tokens already cached
+    hq: int
+    hkv: int
+    head_dim: int = 64
+    page_size: int = 16
+    causal: bool = True
+    window: int = 0
+    sink_std: Optional[float] = 2.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+
 CONFIGS = {
     # Tiny causal GQA 4:1, single sequence of 16 tokens, single KV chunk.
     "tiny_causal": VarlenSpec("tiny_causal", batch=1, seqlen=(16, 16), hq=4, hkv=1,
@@ -131,6 +153,11 @@ CONFIGS = {
                                causal=False, sink_std=None, seed=4),
     "embed_sink": VarlenSpec("embed_sink", batch=512, seqlen=(16, 512), hq=16, hkv=16,
                              causal=False, sink_std=1.0, seed=4),
+    # Chunked prefill on the paged cache (the LLM prefill path of "Fast Embeddings on GPUs"):
+    # 8 sequences each append a 2048-token chunk to 0..6144 cached tokens; 64/8 heads as
+    # the prefill workload, 16-token pages.
+    "chunked_prefill": PagedPrefillSpec("chunked_prefill", batch=8, q_len=(2048, 2048), ctx_len=(0, 6144),
+                                        hq=64, hkv=8, page_size=16, sink_std=2.0, seed=5),
 }
 
 
@@ -203,3 +230,46 @@ def make_paged(spec: PagedSpec, kv_lens: Optional[np.ndarray] = None,
     sinks = _sinks(rng, spec.hq, spec.sink_std)
     return dict(q=q, k_cache=k_cache, v_cache=v_cache, page_table=table, kv_lens=lens.astype(np.int32),
                 sinks=sinks, num_pages=pool, max_kv_len=int(lens.max()) if len(lens) else 0)
+
+
+def make_paged_prefill(spec: PagedPrefillSpec, q_lens: Optional[np.ndarray] = None,
+                       ctx_lens: Optional[np.ndarray] = None, max_pages_per_seq: Optional[int] = None) -> dict:
+    """Inputs for chunked prefill against a paged cache.
+
+    Returns q [T, hq, d] bits with cu_seqlens_q int32 [batch + 1] (sequence b owns rows
+    cu[b]:cu[b+1], its q_lens[b] newest tokens), kv_lens int32 [batch] (= ctx + q_len),
+    k_cache / v_cache [num_pages, hkv, page, d] bits, page_table int32
+    [batch, max_pages_per_seq] and sinks fp32 [hq]. Draw order: chunk lengths -> cached
+    lengths -> page permutation -> Q -> K -> V -> sinks. ``q_lens`` / ``ctx_lens`` override
+    the drawn lengths (edge-case tests).
+    """
+    rng = np.random.default_rng(spec.seed)
+    ql = _draw_lengths(rng, spec.batch, spec.q_len)
+    cl = _draw_lengths(rng, spec.batch, spec.ctx_len)
+    if q_lens is not None:
+        ql = np.asarray(q_lens, dtype=np.int32)
+    if ctx_lens is not None:
+        cl = np.asarray(ctx_lens, dtype=np.int32)
+    lens = (ql.astype(np.int64) + cl).astype(np.int32)
+    P = spec.page_size
+    npages_b = (lens.astype(np.int64) + P - 1) // P
+    num_pages = int(npages_b.sum())
+    perm = rng.permutation(num_pages).astype(np.int32)
+    if max_pages_per_seq is None:
+        cap = spec.q_len[1] + spec.ctx_len[1]
+        max_pages_per_seq = max(1, -(-max(cap, int(lens.max()) if len(lens) else 0) // P))
+    table = np.zeros((len(lens), max_pages_per_seq), dtype=np.int32)
+    off = 0
+    for b, n in enumerate(npages_b):
+        table[b, :n] = perm[off:off + n]
+        off += int(n)
+    cu = np.zeros(len(ql) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(ql, dtype=np.int64).astype(np.int32)
+    q = _normal_bf16(rng, (int(cu[-1]), spec.hq, spec.head_dim))
+    pool = max(num_pages, 1)
+    k_cache = _normal_bf16(rng, (pool, spec.hkv, P, spec.head_dim))
+    v_cache = _normal_bf16(rng, (pool, spec.hkv, P, spec.head_dim))
+    sinks = _sinks(rng, spec.hq, spec.sink_std)
+    return dict(q=q, cu_seqlens_q=cu, q_lens=ql, kv_lens=lens, k_cache=k_cache, v_cache=v_cache,
+                page_table=table, sinks=sinks, num_pages=pool,
+                max_q=int(ql.max()) if len(ql) else 0, max_kv_len=int(lens.max()) if len(lens) else 0)
