@@ -18,14 +18,15 @@ import torch
 from .build import LIB_LOAD_PATH as LIB_PATH
 
 __all__ = [
-    "lib", "AttnSinkError", "attn_sink_prefill", "attn_sink_decode_paged", "attn_sink_decode_paged_partials",
+    "lib", "AttnSinkError", "attn_sink_prefill", "attn_sink_prefill_paged", "attn_sink_decode_paged",
+    "attn_sink_decode_paged_partials",
     "attn_sink_decode_workspace_size",
     "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version", "decode_workspace_layout",
     "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
-    "attn_sink_prefill", "attn_sink_decode_paged", "attn_sink_decode_paged_partials",
+    "attn_sink_prefill", "attn_sink_prefill_paged", "attn_sink_decode_paged", "attn_sink_decode_paged_partials",
     "attn_sink_decode_workspace_size", "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version",
 )
 
@@ -41,6 +42,9 @@ _fp = ctypes.c_void_p  # float* / int32_t* passed as raw addresses
 lib.attn_sink_prefill.restype = ctypes.c_int
 lib.attn_sink_prefill.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _f32, _i32, _i32, _vp, _fp, _vp]
+lib.attn_sink_prefill_paged.restype = ctypes.c_int
+lib.attn_sink_prefill_paged.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _fp, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _f32, _i32, _i32, _vp, _fp, _vp]
 lib.attn_sink_decode_paged.restype = ctypes.c_int
 lib.attn_sink_decode_paged.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz, _vp, _fp, _vp]
@@ -141,6 +145,53 @@ def attn_sink_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: 
                                float(softmax_scale), int(bool(causal)), int(window), _ptr(out), _ptr(lse),
                                _stream(stream))
     _raise(st, "attn_sink_prefill")
+    return out, lse
+
+
+def attn_sink_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,
+                            cu_seqlens_q: torch.Tensor, kv_lens: torch.Tensor, sinks: Optional[torch.Tensor],
+                            max_seqlen_q: int, max_kv_len: int, softmax_scale: Optional[float] = None,
+                            causal: bool = True, window: int = 0, out: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """q [total_q, hq, 64] bf16 (each sequence's newest tokens); caches [num_pages, hkv, page_size, 64] bf16;
+    page_table int32 [batch, max_pages]; cu_seqlens_q int32 [batch+1]; kv_lens int32 [batch] (chunk included)."""
+    dev = q.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check(t, n, torch.bfloat16, dev)
+    for t, n in ((page_table, "page_table"), (cu_seqlens_q, "cu_seqlens_q"), (kv_lens, "kv_lens")):
+        _check(t, n, torch.int32, dev)
+    if sinks is not None:
+        _check(sinks, "sinks", torch.float32, dev)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape or k_cache.shape[3] != q.shape[2]:
+        raise ValueError(f"expected q [T, hq, d] and caches [pages, hkv, page_size, d]; got {tuple(q.shape)}, "
+                         f"{tuple(k_cache.shape)}, {tuple(v_cache.shape)}")
+    total_q, hq, d = q.shape
+    num_pages, hkv, page_size = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    batch = cu_seqlens_q.numel() - 1
+    if kv_lens.numel() != batch or page_table.dim() != 2 or page_table.shape[0] != batch:
+        raise ValueError("kv_lens must be [batch] and page_table [batch, max_pages] with batch = len(cu_seqlens_q) - 1")
+    if sinks is not None and sinks.numel() != hq:
+        raise ValueError(f"sinks must have {hq} entries")
+    if out is not None:
+        _check(out, "out", torch.bfloat16, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, dev)
+        if lse.shape != (total_q, hq):
+            raise ValueError(f"lse must be [{total_q}, {hq}]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev)
+    st = lib.attn_sink_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), page_table.shape[1],
+                                     num_pages, _ptr(cu_seqlens_q), _ptr(kv_lens), _ptr(sinks), batch, total_q,
+                                     int(max_seqlen_q), int(max_kv_len), hq, hkv, d, page_size, float(softmax_scale),
+                                     int(bool(causal)), int(window), _ptr(out), _ptr(lse), _stream(stream))
+    _raise(st, "attn_sink_prefill_paged")
     return out, lse
 
 

@@ -102,7 +102,7 @@ attn_sink_status attn_sink_prefill(const void* q, const void* k, const void* v, 
   const int64_t tiles = ((int64_t)max_seqlen_q + tok - 1) / tok;
   if (tiles * batch * num_kv_heads * (group / gp) + 8 > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
 
-  PrefillParams p;
+  PrefillParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
@@ -122,6 +122,58 @@ attn_sink_status attn_sink_prefill(const void* q, const void* k, const void* v, 
   p.causal = causal != 0;
   p.window = window > 0 ? window : 0;
   p.scale_log2 = softmax_scale * kLog2e;
+  return hip_status(launch_prefill(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+attn_sink_status attn_sink_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+                                         const int32_t* cu_seqlens_q, const int32_t* kv_lens, const float* sinks,
+                                         int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_kv_len,
+                                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t page_size, float softmax_scale, int32_t causal, int32_t window,
+                                         void* out, float* lse, void* stream) {
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_kv_len < 0 || max_pages_per_seq < 1 || num_pages < 1)
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kSupportedHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size < 16 || page_size > 256) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || page_table == nullptr || kv_lens == nullptr ||
+      cu_seqlens_q == nullptr || out == nullptr)
+    return ATTN_SINK_ERR_INVALID_ARG;
+  // One sequence's Q rows are addressed with 32-bit byte offsets.
+  if ((int64_t)max_seqlen_q * num_q_heads * kSupportedHeadDim * 2 > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int32_t gp = prefill_heads_per_tile(group);
+  const int64_t tok = 128 * prefill_row_blocks(max_seqlen_q, gp) / gp;
+  const int64_t tiles = ((int64_t)max_seqlen_q + tok - 1) / tok;
+  if (tiles * batch * num_kv_heads * (group / gp) + 8 > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
+
+  PrefillParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_cache);
+  p.v = static_cast<const uint16_t*>(v_cache);
+  p.sinks = sinks;
+  p.cu_q = cu_seqlens_q;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.batch = batch;
+  p.total_q = total_q;
+  p.max_q = max_seqlen_q;
+  p.max_kv = max_kv_len;
+  p.hq = num_q_heads;
+  p.hkv = num_kv_heads;
+  p.group = group;
+  p.causal = causal != 0;
+  p.window = window > 0 ? window : 0;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.page_table = page_table;
+  p.kv_lens = kv_lens;
+  p.max_pages = max_pages_per_seq;
+  p.num_pages = num_pages;
+  p.page_size = page_size;
+  p.page_shift = ilog2(page_size);
   return hip_status(launch_prefill(p, reinterpret_cast<hipStream_t>(stream)));
 }
 

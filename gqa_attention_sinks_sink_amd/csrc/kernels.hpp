@@ -46,6 +46,12 @@ struct PrefillParams {
   float scale_log2;
   int units;        // work units per (sequence, head group); set by the launcher
   int pair_blocks;  // causal pairing of row blocks u and n-1-u; set by the launcher
+  // Paged K/V (chunked prefill) when page_table != nullptr: k and v are caches
+  // [num_pages, hkv, page_size, 64], sequence b holds kv_lens[b] tokens (its queries are the
+  // newest ones) and cu_kv / total_kv are unused.
+  const int32_t* page_table;  // [batch, max_pages]
+  const int32_t* kv_lens;     // [batch]
+  int max_pages, num_pages, page_size, page_shift;
 };
 
 hipError_t launch_decode_split(const DecodeParams& p, int max_chunks, hipStream_t stream);

@@ -44,7 +44,7 @@ constexpr int kStageBytes = 2 * kTileBytes;        // K then V
 constexpr float kSumGuard = 4294967296.f;  // fast-path bound (2^32) on a lane's sum of exp2(s - m)
 }  // namespace
 
-template <int GP, int RB>
+template <int GP, int RB, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) {
   constexpr int ROWS = 128 * RB;  // rows per workgroup
   constexpr int TOK = ROWS / GP;  // query tokens per workgroup
@@ -84,10 +84,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Sequence bounds, clamped into the declared buffer sizes.
   const int q0 = clampi(p.cu_q[b], 0, p.total_q);
   const int q1 = clampi(p.cu_q[b + 1], q0, p.total_q);
-  const int k0 = clampi(p.cu_kv[b], 0, p.total_kv);
-  const int k1 = clampi(p.cu_kv[b + 1], k0, p.total_kv);
+  int k0 = 0, Lk;
+  if constexpr (PAGED) {
+    Lk = min(clampi(p.kv_lens[b], 0, p.max_kv), p.max_pages << p.page_shift);
+  } else {
+    k0 = clampi(p.cu_kv[b], 0, p.total_kv);
+    const int k1 = clampi(p.cu_kv[b + 1], k0, p.total_kv);
+    Lk = min(k1 - k0, p.max_kv);
+  }
   const int Lq = min(q1 - q0, p.max_q);
-  const int Lk = min(k1 - k0, p.max_kv);
   const int off = Lk - Lq;  // absolute position of query token t is off + t
   const float c = p.scale_log2;
   const int n_blk = (Lq + TOK - 1) / TOK;
@@ -201,6 +206,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // loads are hidden from the compiler (its own tracking would wait for all of them before
   // any LDS read); the waits below retire them explicitly.
   auto issue_tile = [&](int jt, int st) {
+    if constexpr (PAGED) {
+      // Rows [16w, 16w + 16) of the tile are 16 consecutive keys inside one page (pages hold
+      // a power of two >= 16 keys): one 2 KB block of K and one of V for this KV head. The
+      // buffer range stops at the sequence's last key, so rows past it read as zeros.
+      const int kr = jt + 16 * w;
+      const int slot = min(kr >> p.page_shift, p.max_pages - 1);
+      const int pid = clampi(p.page_table[(size_t)b * p.max_pages + slot], 0, p.num_pages - 1);
+      const uint32_t valid = (uint32_t)clampi(Lk - kr, 0, 16);
+      const size_t blk = (((size_t)pid * p.hkv + kvh) * p.page_size + (kr & (p.page_size - 1))) * kHeadDim;
+      const __amdgpu_buffer_rsrc_t pk_r = make_rsrc_uniform(p.k + blk, valid * (kHeadDim * 2));
+      const __amdgpu_buffer_rsrc_t pv_r = make_rsrc_uniform(p.v + blk, valid * (kHeadDim * 2));
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int rr = 8 * ii + (lane >> 3);  // row inside the block
+        const int r = 16 * w + rr;            // row inside the tile
+        const int pch = lane & 7;
+        unsigned char* dst = kv_lds[st] + (16 * w + 8 * ii) * 128;
+        buffer_load16_lds_async(pk_r, dst, (uint32_t)(rr * 128 + ((pch ^ ((r >> 1) & 7)) << 4)));
+        buffer_load16_lds_async(pv_r, dst + kTileBytes, (uint32_t)(rr * 128 + ((pch ^ (((r >> 1) & 1) * 4)) << 4)));
+      }
+      return;
+    }
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int r = 16 * w + 8 * ii + (lane >> 3);
@@ -809,7 +836,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 namespace {
-template <int RB>
+template <int RB, bool PAGED>
 hipError_t launch_rb(PrefillParams p, int gp, hipStream_t stream) {
   const int tok = 128 * RB / gp;
   const int n_blk = (p.max_q + tok - 1) / tok;
@@ -818,11 +845,11 @@ hipError_t launch_rb(PrefillParams p, int gp, hipStream_t stream) {
   const long items = (long)p.units * p.batch * p.hkv * (p.group / gp);
   dim3 grid((unsigned)(8 * ((items + 7) / 8))), block(kThreads);
   switch (gp) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<1, RB>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<2, RB>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<4, RB>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<8, RB>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((prefill_kernel<16, RB>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<1, RB, PAGED>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<2, RB, PAGED>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<4, RB, PAGED>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<8, RB, PAGED>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((prefill_kernel<16, RB, PAGED>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }
@@ -860,9 +887,12 @@ int prefill_row_blocks(int max_q, int gp) {
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (p.batch == 0 || p.total_q == 0 || p.max_q == 0) return hipSuccess;
   const int gp = prefill_heads_per_tile(p.group);
+  const bool rb2 = prefill_row_blocks(p.max_q, gp) == 2;
+  // Chunked prefill on a paged cache: the 4-wave kernel with per-page K/V loads.
+  if (p.page_table != nullptr) return rb2 ? launch_rb<2, true>(p, gp, stream) : launch_rb<1, true>(p, gp, stream);
   // Long sequences without a window: the 8-wave ping-pong kernel.
   if (p.window == 0 && p.max_q >= 2048) return launch_pp(p, gp, stream);
-  return prefill_row_blocks(p.max_q, gp) == 2 ? launch_rb<2>(p, gp, stream) : launch_rb<1>(p, gp, stream);
+  return rb2 ? launch_rb<2, false>(p, gp, stream) : launch_rb<1, false>(p, gp, stream);
 }
 
 }  // namespace attn_sink

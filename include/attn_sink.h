@@ -98,6 +98,37 @@ attn_sink_status attn_sink_prefill(
     void* out, float* lse, void* stream);
 
 /*
+ * Chunked prefill against a paged KV cache: each sequence's queries are its newest tokens,
+ * whose K/V (together with the cached context before them) are already in the cache ("Fast
+ * Embeddings on GPUs", attention section: the LLM path runs prefill as well as decode on
+ * paged KV, next to the ragged path of attn_sink_prefill).
+ *
+ *   q            bf16 [total_q, num_q_heads, 64]; sequence b owns rows
+ *                [cu_seqlens_q[b], cu_seqlens_q[b+1]), its Lq_b newest tokens: query token t
+ *                sits at absolute position kv_lens[b] - Lq_b + t.
+ *   k_cache, v_cache, page_table, max_pages_per_seq, num_pages, page_size
+ *                as for attn_sink_decode_paged (HND pages, page_size a power of two in
+ *                [16, 256]).
+ *   cu_seqlens_q int32 [batch + 1] on the device, non-decreasing, starting at 0.
+ *   kv_lens      int32 [batch] on the device: tokens in the cache per sequence, the chunk
+ *                included (clamped to [0, min(max_kv_len, max_pages_per_seq * page_size)]).
+ *   total_q, max_seqlen_q, max_kv_len
+ *                rows in q and host upper bounds of the chunk and cache lengths.
+ *   sinks, softmax_scale, causal, window, out, lse
+ *                as for attn_sink_prefill.
+ * No workspace: every chunk's rows are finished in one pass. Errors as above; one
+ * sequence's Q rows must span less than 2^31 bytes.
+ */
+attn_sink_status attn_sink_prefill_paged(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    const int32_t* cu_seqlens_q, const int32_t* kv_lens, const float* sinks,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_kv_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    float softmax_scale, int32_t causal, int32_t window,
+    void* out, float* lse, void* stream);
+
+/*
  * Paged decode (q_len = 1) and multi-token verify decode (q_len 2..8, causal inside the
  * block) against a paged KV cache, split along the KV length into kv_chunk-token
  * chunks whose partials are merged by log-sum-exp ("GPT-OSS on Day 0", section

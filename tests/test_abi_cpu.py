@@ -79,6 +79,37 @@ def _prefill(amd, **kw):
                                      a["scale"], a["causal"], a["window"], a["out"], a["lse"], a["stream"])
 
 
+def _prefill_paged(amd, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, table=FAKE, max_pages=4, num_pages=8, cu_q=FAKE, lens=FAKE, sinks=None,
+             batch=2, total_q=32, max_q=16, max_kv=64, hq=8, hkv=2, d=64, page=16, scale=0.125, causal=1, window=0,
+             out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return amd.lib.attn_sink_prefill_paged(a["q"], a["kc"], a["vc"], a["table"], a["max_pages"], a["num_pages"],
+                                           a["cu_q"], a["lens"], a["sinks"], a["batch"], a["total_q"], a["max_q"],
+                                           a["max_kv"], a["hq"], a["hkv"], a["d"], a["page"], a["scale"], a["causal"],
+                                           a["window"], a["out"], a["lse"], a["stream"])
+
+
+def test_prefill_paged_argument_errors(amd):
+    assert _prefill_paged(amd, d=128) == UNSUPPORTED
+    assert _prefill_paged(amd, page=8) == UNSUPPORTED
+    assert _prefill_paged(amd, page=24) == UNSUPPORTED
+    assert _prefill_paged(amd, page=512) == UNSUPPORTED
+    assert _prefill_paged(amd, max_q=1 << 18, hq=64, hkv=8) == UNSUPPORTED
+    assert _prefill_paged(amd, hq=6, hkv=4) == INVALID
+    assert _prefill_paged(amd, hkv=0) == INVALID
+    assert _prefill_paged(amd, scale=0.0) == INVALID
+    assert _prefill_paged(amd, scale=float("nan")) == INVALID
+    assert _prefill_paged(amd, batch=-1) == INVALID
+    assert _prefill_paged(amd, max_pages=0) == INVALID
+    assert _prefill_paged(amd, num_pages=0) == INVALID
+    for name in ("q", "kc", "vc", "table", "cu_q", "lens", "out"):
+        assert _prefill_paged(amd, **{name: None}) == INVALID, name
+    # nothing to do: accepted without launching anything
+    assert _prefill_paged(amd, batch=0, q=None) == OK
+    assert _prefill_paged(amd, total_q=0) == OK
+    assert _prefill_paged(amd, max_q=0) == OK
+
 def test_prefill_argument_errors(amd):
     assert _prefill(amd, d=128) == UNSUPPORTED
     assert _prefill(amd, hq=6, hkv=4) == INVALID

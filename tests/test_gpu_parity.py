@@ -11,7 +11,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
-from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_varlen, scaled  # noqa: E402
+from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_paged_prefill, make_varlen, scaled  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -188,6 +188,70 @@ def test_embedding_full_size_sampled(amd, name):
                                    inp["cu_seqlens"], inp["sinks"], spec.scale, False, 0, seqs=[0, 1, 77, 300, 511])
     assert_close(out, lse, ro, rl, name)
 
+
+# -------------------------------------------------------------------------------------------
+# chunked prefill on a paged cache
+# -------------------------------------------------------------------------------------------
+def run_prefill_paged(amd, inp, spec, sinks=True, causal=None, window=None):
+    s = torch.from_numpy(inp["sinks"]).to(DEV) if sinks else None
+    out, lse = amd.attn_sink_prefill_paged(
+        tbits(inp["q"]), tbits(inp["k_cache"]), tbits(inp["v_cache"]), torch.from_numpy(inp["page_table"]).to(DEV),
+        torch.from_numpy(inp["cu_seqlens_q"]).to(DEV), torch.from_numpy(inp["kv_lens"]).to(DEV), s, inp["max_q"],
+        inp["max_kv_len"], spec.scale, spec.causal if causal is None else causal,
+        spec.window if window is None else window)
+    torch.cuda.synchronize()
+    return out_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_prefill_paged(inp, spec, sinks=True, causal=None, window=None, **kw):
+    s = inp["sinks"] if sinks else np.full_like(inp["sinks"], -np.inf)
+    return oracle.prefill_paged(f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"]), inp["page_table"],
+                                inp["cu_seqlens_q"], inp["kv_lens"], s, spec.scale,
+                                spec.causal if causal is None else causal, spec.window if window is None else window,
+                                **kw)
+
+
+@pytest.mark.parametrize("hq,hkv,page_size", [(16, 2, 16), (8, 8, 32), (64, 8, 16), (12, 3, 64), (4, 4, 256)])
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 45), (False, 0)])
+def test_prefill_paged_ragged(amd, hq, hkv, page_size, causal, window):
+    spec = scaled(CONFIGS["chunked_prefill"], batch=4, q_len=(1, 300), ctx_len=(0, 700), hq=hq, hkv=hkv,
+                  page_size=page_size, seed=hq + hkv + page_size)
+    inp = make_paged_prefill(spec)
+    out, lse = run_prefill_paged(amd, inp, spec, causal=causal, window=window)
+    ro, rl = oracle_prefill_paged(inp, spec, causal=causal, window=window)
+    assert_close(out, lse, ro, rl, f"paged prefill hq={hq} hkv={hkv} page={page_size} causal={causal} w={window}")
+
+
+def test_prefill_paged_edge_lengths_and_no_sink(amd):
+    # empty chunks, chunks of one token, no context, context ending mid-page, long single chunk
+    spec = scaled(CONFIGS["chunked_prefill"], batch=6, hq=8, hkv=2, seed=71)
+    inp = make_paged_prefill(spec, q_lens=[0, 1, 64, 65, 0, 1500], ctx_lens=[5, 0, 0, 17, 0, 33])
+    for sinks in (True, False):
+        out, lse = run_prefill_paged(amd, inp, spec, sinks=sinks)
+        ro, rl = oracle_prefill_paged(inp, spec, sinks=sinks)
+        assert_close(out, lse, ro, rl, f"paged prefill edges sinks={sinks}")
+
+
+def test_prefill_paged_page_permutation_bit_identical(amd):
+    spec = scaled(CONFIGS["chunked_prefill"], batch=3, q_len=(100, 400), ctx_len=(0, 900), hq=16, hkv=2, seed=72)
+    inp = make_paged_prefill(spec)
+    a = run_prefill_paged(amd, inp, spec)
+    perm = np.random.default_rng(4).permutation(inp["num_pages"])
+    inv = np.argsort(perm)
+    inp2 = dict(inp)
+    inp2["k_cache"], inp2["v_cache"] = inp["k_cache"][inv], inp["v_cache"][inv]
+    inp2["page_table"] = perm[inp["page_table"]].astype(np.int32)
+    b = run_prefill_paged(amd, inp2, spec)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_prefill_paged_full_size_sampled(amd):
+    spec = CONFIGS["chunked_prefill"]
+    inp = make_paged_prefill(spec)
+    out, lse = run_prefill_paged(amd, inp, spec)
+    rows = {0: [0, 1, 63, 64, 2047], 3: [1000, 2046], 7: [5, 1500, 2047]}
+    ro, rl = oracle_prefill_paged(inp, spec, seqs=list(rows), rows=rows)
+    assert_close(out, lse, ro, rl, "chunked_prefill")
 
 # -------------------------------------------------------------------------------------------
 # paged decode / verify
