@@ -6,7 +6,8 @@ order, 512-token chunks merged by log-sum-exp). One step = one attn_sink_decode_
 (split-KV kernel + merge kernel) over the whole batch, inputs resident in HBM.
 
 Other workloads (--workload): causal_prefill, window_prefill, verify, embed (two passes:
-sinks disabled, then N(0,1) sinks), tiny_causal.
+sinks disabled, then N(0,1) sinks), chunked_prefill (2048-token chunks appended to paged
+caches of 0..6144 tokens), tiny_causal.
 
 Prints ONE JSON line. ``value`` is the algorithmic rate of the whole step (GB/s for the
 memory-bound paths, TFLOP/s for prefill); ``roofline`` describes the dominant kernel, timed
@@ -27,7 +28,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_varlen  # noqa: E402
+from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_paged_prefill, make_varlen  # noqa: E402
 
 METRIC = "sink-attn decode HBM GB/s (% peak); prefill TFLOP/s (% bf16 MFMA peak)"
 HBM_PEAK_GBS = 8000.0
@@ -44,7 +45,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="paged_decode",
-                    choices=["paged_decode", "verify", "causal_prefill", "window_prefill", "embed", "tiny_causal"])
+                    choices=["paged_decode", "verify", "causal_prefill", "window_prefill", "embed", "chunked_prefill",
+                             "tiny_causal"])
     ap.add_argument("--kv-chunk", type=int, default=None,
                     help="split-KV chunk length for the paged workloads (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU oracle sample (wall seconds)")
@@ -110,6 +112,8 @@ def prefill_kernel_name(spec, max_seqlen):
 def dominant_kernel(name):
     if name in ("paged_decode", "verify"):
         return "decode_split_kernel"
+    if name == "chunked_prefill":
+        return "prefill_kernel"  # paged K/V always run on the 4-wave kernel
     spec = CONFIGS["embed_sink" if name == "embed" else name]
     return prefill_kernel_name(spec, spec.seqlen[1])
 
@@ -405,6 +409,105 @@ def bench_varlen(args, torch, amd, name):
     return res
 
 
+def chunk_pairs(q_lens, kv_lens, causal, window):
+    """Visible (query, key) pairs per sequence of a chunked prefill (queries are the newest
+    q_len of kv_len tokens)."""
+    out = []
+    for lq, lk in zip(np.asarray(q_lens, dtype=np.int64), np.asarray(kv_lens, dtype=np.int64)):
+        pos = np.arange(lk - lq, lk)
+        vis = np.minimum(pos + 1, lk) if causal else np.full(lq, lk)
+        if window > 0:
+            vis = np.minimum(vis, window)
+        out.append(int(vis.sum()))
+    return np.asarray(out, dtype=np.int64)
+
+
+def cpu_baseline_chunked(inp, spec, seconds, sinks, block=64):
+    """The fp64 oracle on blocks of 64 chunk rows, cycling over sequences."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    f64 = lambda b: bf16_bits_to_f32(b).astype(np.float64)
+    cu, lens = inp["cu_seqlens_q"], inp["kv_lens"]
+    q, kc, vc = f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"])  # input widening, not timed
+    done, n = 0.0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < seconds:
+            b = n % len(lens)
+            q0, lq = int(cu[b]), int(cu[b + 1] - cu[b])
+            rows = np.arange(min(block, lq))
+            # one sequence at a time, as the varlen baseline does
+            oracle.prefill_paged(q[q0:q0 + lq], kc, vc, inp["page_table"][b:b + 1], np.array([0, lq]), lens[b:b + 1],
+                                 sinks, spec.scale, spec.causal, spec.window, rows={0: rows})
+            pos = int(lens[b]) - lq + rows
+            vis = np.minimum(pos + 1, int(lens[b])) if spec.causal else np.full(len(rows), int(lens[b]))
+            if spec.window > 0:
+                vis = np.minimum(vis, spec.window)
+            done += float(vis.sum()) * 4 * 64 * spec.hq
+            n += 1
+    dt = time.perf_counter() - t0
+    return done / dt / 1e12, n, dt
+
+
+def bench_chunked(args, torch, amd, name):
+    spec = CONFIGS[name]
+    inp = make_paged_prefill(spec)
+    dev = torch.device("cuda:0")
+    q, kc, vc = (tbits(torch, inp[x], dev) for x in ("q", "k_cache", "v_cache"))
+    table = torch.from_numpy(inp["page_table"]).to(dev)
+    cu = torch.from_numpy(inp["cu_seqlens_q"]).to(dev)
+    lens = torch.from_numpy(inp["kv_lens"]).to(dev)
+    sinks = torch.from_numpy(inp["sinks"]).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], spec.hq), dtype=torch.float32, device=dev)
+
+    def step():
+        amd.attn_sink_prefill_paged(q, kc, vc, table, cu, lens, sinks, inp["max_q"], inp["max_kv_len"], spec.scale,
+                                    spec.causal, spec.window, out=out, lse=lse)
+
+    pairs = chunk_pairs(inp["q_lens"], inp["kv_lens"], spec.causal, spec.window)
+    flops_seq = pairs * 4 * 64 * spec.hq
+    flops = int(flops_seq.sum())
+    T = int(inp["q_lens"].sum())
+    kv_tokens = int(inp["kv_lens"].astype(np.int64).sum())
+    pages = int(((inp["kv_lens"].astype(np.int64) + spec.page_size - 1) // spec.page_size).sum())
+    algo_bytes = T * (spec.hq * 64 * 2 * 2 + spec.hq * 4) + kv_tokens * spec.hkv * 64 * 2 * 2 + 4 * pages
+
+    ms = time_calls(torch, step, args.steps, args.warmup)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    bound = "mfma" if flops / algo_bytes > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm"
+    if bound == "mfma":
+        roof = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": "prefill_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = measured_traffic(name, "prefill")
+    roof["algorithmic_flops_per_launch"] = flops
+    roof["algorithmic_bytes_per_launch"] = algo_bytes
+    roof["kernel_ms"] = round(ms, 5)
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: {spec.batch} seqs, chunks of {spec.q_len[0]}..{spec.q_len[1]} tokens on "
+                               f"{spec.ctx_len[0]}..{spec.ctx_len[1]} cached (sum {T} queries, {kv_tokens} keys), "
+                               f"{spec.hq}/{spec.hkv} heads, d 64, {spec.page_size}-token pages, causal={spec.causal}",
+                   "algorithmic_flops": flops, "algorithmic_bytes": algo_bytes},
+        "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2), "gb_per_s": round(gbs, 1),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        v, n, dt = cpu_baseline_chunked(inp, spec, args.cpu_seconds, inp["sinks"])
+        res["cpu_baseline"] = {"value": round(v, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} blocks of 64 chunk rows (cycling over the sequences), {dt:.1f} s wall, "
+                                         f"fp64 NumPy, BLAS limited to 1 thread"}
+    return res
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -429,6 +532,8 @@ def main():
         return
     if args.workload in ("paged_decode", "verify"):
         res = bench_paged(args, torch, amd, args.workload)
+    elif args.workload == "chunked_prefill":
+        res = bench_chunked(args, torch, amd, args.workload)
     else:
         res = bench_varlen(args, torch, amd, args.workload)
     print(json.dumps(res), flush=True)
