@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // instead of both waves alternating between the two kinds of work on their own.
 // K/V tiles (64 keys) go through a 4-stage LDS ring: tile t is read in slots 2t .. 2t + 3 and
 // is loaded (buffer loads straight into LDS) during slots 2t - 4 .. 2t - 1.
-template <int GP>
+template <int GP, bool PAGED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_pp_kernel(PrefillParams p) {
   constexpr int RB = 2;
   constexpr int NW = 8;
@@ -474,10 +474,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int q0 = clampi(p.cu_q[b], 0, p.total_q);
   const int q1 = clampi(p.cu_q[b + 1], q0, p.total_q);
-  const int k0 = clampi(p.cu_kv[b], 0, p.total_kv);
-  const int k1 = clampi(p.cu_kv[b + 1], k0, p.total_kv);
+  int k0 = 0, Lk;
+  if constexpr (PAGED) {
+    Lk = min(clampi(p.kv_lens[b], 0, p.max_kv), p.max_pages << p.page_shift);
+  } else {
+    k0 = clampi(p.cu_kv[b], 0, p.total_kv);
+    const int k1 = clampi(p.cu_kv[b + 1], k0, p.total_kv);
+    Lk = min(k1 - k0, p.max_kv);
+  }
   const int Lq = min(q1 - q0, p.max_q);
-  const int Lk = min(k1 - k0, p.max_kv);
   const int off = Lk - Lq;
   const float c = p.scale_log2;
   const int n_blk = (Lq + TOK - 1) / TOK;
@@ -577,6 +582,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // registers across the pass, it would be spilled, and each reload would wait for every
     // tile in flight.
     auto issue_tile = [&](int t) {
+      if constexpr (PAGED) {
+        // Rows [8w, 8w + 8) of the tile are 8 consecutive keys inside one page (pages hold a
+        // power of two >= 16 keys); the buffer range ends at the sequence's last key.
+        const int kr = jb + t * kTileN + 8 * w;
+        const int slot = min(kr >> p.page_shift, p.max_pages - 1);
+        const int pid = clampi(p.page_table[(size_t)b * p.max_pages + slot], 0, p.num_pages - 1);
+        const uint32_t valid = (uint32_t)clampi(Lk - kr, 0, 8);
+        const size_t blk = (((size_t)pid * p.hkv + kvh) * p.page_size + (kr & (p.page_size - 1))) * kHeadDim;
+        const int ln = opaque_lane_id();
+        const int r8 = ln >> 3;
+        const int pch = ln & 7;
+        const int swz_k = (r8 >> 1) | ((w & 1) << 2);
+        const int swz_v = (r8 & 2) << 1;
+        unsigned char* dst = kv_lds[t & (kRing - 1)] + 8 * w * 128;
+        buffer_load16_lds_async(make_rsrc_uniform(p.k + blk, valid * (kHeadDim * 2)), dst,
+                                (uint32_t)(r8 * 128 + ((pch ^ swz_k) << 4)));
+        buffer_load16_lds_async(make_rsrc_uniform(p.v + blk, valid * (kHeadDim * 2)), dst + kTileBytes,
+                                (uint32_t)(r8 * 128 + ((pch ^ swz_v) << 4)));
+        return;
+      }
       const int ln = opaque_lane_id();
       const int r8 = ln >> 3;  // row 8 w + r8 of the tile
       const int pch = ln & 7;
@@ -854,6 +879,7 @@ hipError_t launch_rb(PrefillParams p, int gp, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool PAGED>
 hipError_t launch_pp(PrefillParams p, int gp, hipStream_t stream) {
   const int tok = 512 / gp;
   const int n_blk = (p.max_q + tok - 1) / tok;
@@ -862,11 +888,11 @@ hipError_t launch_pp(PrefillParams p, int gp, hipStream_t stream) {
   const long items = (long)p.units * p.batch * p.hkv * (p.group / gp);
   dim3 grid((unsigned)(8 * ((items + 7) / 8))), block(512);
   switch (gp) {
-    case 1: hipLaunchKernelGGL((prefill_pp_kernel<1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((prefill_pp_kernel<2>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((prefill_pp_kernel<4>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((prefill_pp_kernel<8>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((prefill_pp_kernel<16>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((prefill_pp_kernel<1, PAGED>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((prefill_pp_kernel<2, PAGED>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((prefill_pp_kernel<4, PAGED>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((prefill_pp_kernel<8, PAGED>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((prefill_pp_kernel<16, PAGED>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }
@@ -888,10 +914,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (p.batch == 0 || p.total_q == 0 || p.max_q == 0) return hipSuccess;
   const int gp = prefill_heads_per_tile(p.group);
   const bool rb2 = prefill_row_blocks(p.max_q, gp) == 2;
-  // Chunked prefill on a paged cache: the 4-wave kernel with per-page K/V loads.
-  if (p.page_table != nullptr) return rb2 ? launch_rb<2, true>(p, gp, stream) : launch_rb<1, true>(p, gp, stream);
-  // Long sequences without a window: the 8-wave ping-pong kernel.
-  if (p.window == 0 && p.max_q >= 2048) return launch_pp(p, gp, stream);
+  const bool paged = p.page_table != nullptr;  // chunked prefill on a paged cache
+  // Long query ranges without a window: the 8-wave ping-pong kernel.
+  if (p.window == 0 && p.max_q >= 2048) return paged ? launch_pp<true>(p, gp, stream) : launch_pp<false>(p, gp, stream);
+  if (paged) return rb2 ? launch_rb<2, true>(p, gp, stream) : launch_rb<1, true>(p, gp, stream);
   return rb2 ? launch_rb<2, false>(p, gp, stream) : launch_rb<1, false>(p, gp, stream);
 }
 

@@ -232,6 +232,17 @@ def test_prefill_paged_edge_lengths_and_no_sink(amd):
         assert_close(out, lse, ro, rl, f"paged prefill edges sinks={sinks}")
 
 
+@pytest.mark.parametrize("hq,hkv,page_size,causal", [(8, 1, 16, True), (16, 16, 64, True), (12, 3, 32, False)])
+def test_prefill_paged_long_chunks(amd, hq, hkv, page_size, causal):
+    # chunks of 2048+ tokens run on the 8-wave kernel
+    spec = scaled(CONFIGS["chunked_prefill"], batch=3, q_len=(2048, 2200), ctx_len=(0, 700), hq=hq, hkv=hkv,
+                  page_size=page_size, seed=80 + hq)
+    inp = make_paged_prefill(spec, ctx_lens=[0, 37, 700])
+    out, lse = run_prefill_paged(amd, inp, spec, causal=causal)
+    rows = {b: [0, 1, 63, 64, 511, 512, 1000, 2047, int(inp["q_lens"][b]) - 1] for b in range(3)}
+    ro, rl = oracle_prefill_paged(inp, spec, causal=causal, seqs=list(rows), rows=rows)
+    assert_close(out, lse, ro, rl, f"long paged chunks hq={hq} hkv={hkv} page={page_size} causal={causal}")
+
 def test_prefill_paged_page_permutation_bit_identical(amd):
     spec = scaled(CONFIGS["chunked_prefill"], batch=3, q_len=(100, 400), ctx_len=(0, 900), hq=16, hkv=2, seed=72)
     inp = make_paged_prefill(spec)
