@@ -113,7 +113,8 @@ def dominant_kernel(name):
     if name in ("paged_decode", "verify"):
         return "decode_split_kernel"
     if name == "chunked_prefill":
-        return "prefill_kernel"  # paged K/V always run on the 4-wave kernel
+        spec = CONFIGS[name]
+        return "prefill_pp_kernel" if (spec.window <= 0 and spec.q_len[1] >= 2048) else "prefill_kernel"
     spec = CONFIGS["embed_sink" if name == "embed" else name]
     return prefill_kernel_name(spec, spec.seqlen[1])
 
@@ -477,12 +478,12 @@ def bench_chunked(args, torch, amd, name):
     tflops = flops / (ms * 1e-3) / 1e12
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     bound = "mfma" if flops / algo_bytes > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm"
+    kname = "prefill_pp_kernel" if (spec.window <= 0 and inp["max_q"] >= 2048) else "prefill_kernel"
     if bound == "mfma":
-        roof = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        roof = {"kernel": kname, "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
     else:
-        roof = {"kernel": "prefill_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
+        roof = {"kernel": kname, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(name, "prefill")
     roof["algorithmic_flops_per_launch"] = flops
