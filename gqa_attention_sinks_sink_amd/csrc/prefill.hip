@@ -450,8 +450,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int TOK = ROWS / GP;
   constexpr int kRing = 4;
   __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[kRing][kStageBytes];
-  // Per-wave staging of the output rows (64 rows x 128 bytes per wave).
-  __shared__ __attribute__((aligned(16))) unsigned char out_lds[NW][64 * kHeadDim * 2];
+  // Per-wave slice (64 rows x 128 bytes): the wave's Q rows during a pass, then its output rows.
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds[NW][64 * kHeadDim * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -520,29 +520,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     vl = 0;
     if (vh < vl) vh = vl;
   };
-  // Q rows of the pass. Rows past the end load the last valid row (their results are never
-  // stored). The loads are untracked, so that waiting for them does not also wait for the K/V
-  // tiles issued after them; they have landed once the first tile has, where qb is tied.
-  u32x4 qb[RB][4];
+  // The wave's 64 Q rows of the pass go to its LDS slice by DMA, issued before the first
+  // K/V tiles (so they have landed once tile 0 has); 16-byte chunk c of row i sits at chunk
+  // position c ^ ((i >> 1) & 7), as for K. Rows past the end load the last valid row (their
+  // results are never stored). Q lives in LDS, not in registers, for the whole pass.
+  unsigned char* qw = q_lds[w];
   {
     const int ln = opaque_lane_id();
+    const int pos = ln & 7;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int r = (w * RB + rb) * 32 + (ln & 31);
+    for (int k = 0; k < 8; ++k) {
+      const int i = 8 * k + (ln >> 3);
+      const int r = 64 * w + i;
       const int t = min(ts + r / GP, te - 1);
-      const uint32_t voff = ((uint32_t)t * p.hq + head0 + (r % GP)) * (kHeadDim * 2) + (ln >> 5) * 16;
-      qb[rb][0] = buffer_load16_untracked<0>(rq, voff);
-      qb[rb][1] = buffer_load16_untracked<32>(rq, voff);
-      qb[rb][2] = buffer_load16_untracked<64>(rq, voff);
-      qb[rb][3] = buffer_load16_untracked<96>(rq, voff);
+      const int c = pos ^ ((i >> 1) & 7);
+      buffer_load16_lds_async(rq, qw + 8 * k * 128,
+                              ((uint32_t)t * p.hq + head0 + (r % GP)) * (kHeadDim * 2) + (uint32_t)(c * 16));
     }
   }
-  auto tie_q = [&]() {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) tie(qb[rb][ks]);
-  };
   float m[RB], lsum[RB];
   f32x16 o[RB][2];
   int hi_min = 0x7fffffff, lo_max = -0x7fffffff;
@@ -645,7 +640,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // The phases of one wave stay apart: letting the scheduler hoist this phase's LDS reads
       // into the softmax phase would keep S, P and all fragments live at once.
       __builtin_amdgcn_sched_barrier(0);
-      u32x4 av[4][2], ka[2][4];
+      u32x4 av[4][2], ka[2][4], qa[RB][4];
       if constexpr (do_pv) {
         const unsigned char* vt = kv_lds[(t - 1) & (kRing - 1)] + kTileBytes;
 #pragma unroll
@@ -660,6 +655,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) ka[kt][ks] = *reinterpret_cast<const u32x4*>(kt_lds + kt * 4096 + k_off[ks]);
+        // Q^T fragments: the same lane layout as K (row r32 of a 32-row block).
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) qa[rb][ks] = *reinterpret_cast<const u32x4*>(qw + rb * 4096 + k_off[ks]);
       }
       // Keep the PV products ahead of the QK products: interleaving them would keep P, S and
       // both sets of fragments live at once.
@@ -681,7 +681,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-              s[rb][kt] = mfma32(as_bf16x8(ka[kt][ks]), as_bf16x8(qb[rb][ks]), ks == 0 ? f32x16{} : s[rb][kt]);
+              s[rb][kt] = mfma32(as_bf16x8(ka[kt][ks]), as_bf16x8(qa[rb][ks]), ks == 0 ? f32x16{} : s[rb][kt]);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -786,7 +786,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const std::false_type no{};
     if (lag) sync_slot(0);
     sync_slot(lag);
-    tie_q();
     prio_matrix();
     matrix_phase(0, no, yes);
     sync_slot(1 + lag);
@@ -810,10 +809,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // next pass reuses it.
     __syncthreads();
   } else {
-    // No key is visible: Q is not needed, but its registers must not be reused before the
-    // loads have landed.
+    // No key is visible: Q is not needed, but its DMA must land before the slice is reused
+    // for the output.
     WAIT_VMCNT(0);
-    tie_q();
   }
 
   // O goes through this wave's LDS slice: the accumulator layout gives a lane 8-byte pieces
@@ -822,7 +820,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   {
     const int ln = opaque_lane_id();
     const int hf = ln >> 5;
-    unsigned char* ow = out_lds[w];
+    unsigned char* ow = qw;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float lt = lsum[rb] + shfl_xor(lsum[rb], 32);
