@@ -22,5 +22,6 @@ pages: a stated reading).
 """
 from .attention import (  # noqa: F401
     attend, attention_weights, prefill_varlen, gather_pages, decode_paged, prefill_paged,
+    tree_visible, decode_paged_tree,
     online_partials, split_decode, merge, plan_chunks,
 )

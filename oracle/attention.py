@@ -47,19 +47,24 @@ def _visible(q_pos: np.ndarray, lk: int, causal: bool, window: int) -> np.ndarra
 
 def attention_weights(q: np.ndarray, k: np.ndarray, sink: float, scale: float,
                       causal: bool, window: int,
-                      q_pos: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                      q_pos: Optional[np.ndarray] = None,
+                      visible: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Softmax over [scores, sink] for ONE head of ONE sequence.
 
     q [lq, d], k [lk, d] (fp64). Returns (w [lq, lk], w_sink [lq], lse [lq]) with
     w[t, j] = e^{s_tj - M_t} / D_t for visible keys (0 otherwise), w_sink = e^{sink - M_t} / D_t,
     M_t = max(max_j s_tj, sink), D_t = sum_j e^{s_tj - M_t} + e^{sink - M_t}, lse = M_t + ln D_t.
-    ``q_pos`` gives the absolute query positions (default: the last lq of lk positions).
+    ``q_pos`` gives the absolute query positions (default: the last lq of lk positions);
+    ``visible`` (bool [lq, lk]), when given, is the mask itself and replaces causal/window.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     lq, lk = q.shape[0], k.shape[0]
     s = scale * (q @ k.T) if lk else np.zeros((lq, 0))
-    vis = _visible(_positions(lq, lk) if q_pos is None else q_pos, lk, causal, window)
+    if visible is not None:
+        vis = np.asarray(visible, dtype=bool)
+    else:
+        vis = _visible(_positions(lq, lk) if q_pos is None else q_pos, lk, causal, window)
     s_vis = np.where(vis, s, -np.inf)
     sink = float(sink)
     row_max = s_vis.max(axis=1) if lk else np.full(lq, -np.inf)
@@ -81,7 +86,7 @@ def attention_weights(q: np.ndarray, k: np.ndarray, sink: float, scale: float,
 
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, sinks: np.ndarray, scale: float,
            causal: bool, window: int = 0, heads: Optional[Sequence[int]] = None,
-           q_pos: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+           q_pos: Optional[np.ndarray] = None, visible: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Sink attention for ONE sequence.
 
     q [lq, hq, d], k/v [lk, hkv, d], sinks [hq] (fp32 or fp64, -inf disables a head's sink).
@@ -99,7 +104,7 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, sinks: np.ndarray, scale
     lse = np.full((lq, hq), np.nan)
     for h in (range(hq) if heads is None else heads):
         g = h // group
-        w, _, l = attention_weights(q[:, h, :], k[:, g, :], float(sinks[h]), scale, causal, window, q_pos)
+        w, _, l = attention_weights(q[:, h, :], k[:, g, :], float(sinks[h]), scale, causal, window, q_pos, visible)
         out[:, h, :] = w @ v[:, g, :] if k.shape[0] else 0.0
         lse[:, h] = l
     return out, lse
@@ -163,6 +168,43 @@ def decode_paged(q, k_cache, v_cache, page_table, kv_lens, sinks, q_len, scale, 
         out[b * q_len:(b + 1) * q_len], lse[b * q_len:(b + 1) * q_len] = o, l
     return out, lse
 
+
+def tree_visible(tree_mask_rows: np.ndarray, q_len: int, lk: int, window: int = 0) -> np.ndarray:
+    """Visibility [q_len, lk] of a draft tree verified in one step ("Accelerating Sonar through
+    speculation", EAGLE section: tree-shaped drafts need a custom attention mask). The q_len
+    draft tokens are the last q_len of lk tokens; row t sees every earlier (prefix) token and
+    the draft tokens i whose bit i is set in tree_mask_rows[t]; a window W > 0 also bounds
+    every key by position (p - j < W)."""
+    p = (lk - q_len) + np.arange(q_len)
+    j = np.arange(lk)
+    vis = np.zeros((q_len, lk), dtype=bool)
+    vis[:, :lk - q_len] = True
+    bits = np.asarray(tree_mask_rows, dtype=np.int64)
+    for t in range(q_len):
+        for i in range(q_len):
+            vis[t, lk - q_len + i] = bool((bits[t] >> i) & 1)
+    if window > 0:
+        vis &= (p[:, None] - j[None, :]) < window
+    return vis
+
+
+def decode_paged_tree(q, k_cache, v_cache, page_table, kv_lens, tree_mask, sinks, q_len, scale, window=0,
+                      seqs: Optional[Sequence[int]] = None):
+    """Verification of a draft tree against a paged cache. q [batch * q_len, hq, d]; tree_mask
+    int [batch * q_len] bitmaps (bit i of row b * q_len + t: draft token i visible to token t).
+    Returns out, lse (rows of sequences not in ``seqs`` are NaN)."""
+    batch = len(kv_lens)
+    rows, hq, d = q.shape
+    out = np.full((rows, hq, d), np.nan)
+    lse = np.full((rows, hq), np.nan)
+    for b in (range(batch) if seqs is None else seqs):
+        L = int(kv_lens[b])
+        kb = gather_pages(k_cache, page_table[b], L)
+        vb = gather_pages(v_cache, page_table[b], L)
+        vis = tree_visible(tree_mask[b * q_len:(b + 1) * q_len], q_len, L, window)
+        o, l = attend(q[b * q_len:(b + 1) * q_len], kb, vb, sinks, scale, True, window, visible=vis)
+        out[b * q_len:(b + 1) * q_len], lse[b * q_len:(b + 1) * q_len] = o, l
+    return out, lse
 
 def prefill_paged(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, sinks, scale, causal, window=0,
                   seqs: Optional[Sequence[int]] = None, rows: Optional[dict] = None):

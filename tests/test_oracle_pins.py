@@ -16,7 +16,8 @@ import torch
 import mpmath
 
 import oracle
-from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_paged_prefill, make_varlen, scaled
+from workloads import (CONFIGS, bf16_bits_to_f32, make_paged, make_paged_prefill, make_tree_masks, make_varlen,
+                       scaled)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_derived.json")
 
@@ -344,6 +345,81 @@ def test_paged_prefill_uniform_chunks_equal_decode_paged():
     b = oracle.decode_paged(q, kc, vc, inp["page_table"], inp["kv_lens"], inp["sinks"], 5, spec.scale, True, 0)
     np.testing.assert_allclose(a[0], b[0], atol=1e-13, rtol=0)
     np.testing.assert_allclose(a[1], b[1], atol=1e-13, rtol=0)
+
+# ---------------------------------------------------------------------------------------
+# c-P8c: tree-mask verification
+# ---------------------------------------------------------------------------------------
+def _tree_inputs(seed, batch=3, q_len=6, kv=(20, 90), hq=8, hkv=2):
+    spec = scaled(CONFIGS["tree_verify"], batch=batch, q_len=q_len, kv_len=kv, hq=hq, hkv=hkv, seed=seed)
+    inp = make_paged(spec)
+    return spec, inp, _f64(inp["q"]), _f64(inp["k_cache"]), _f64(inp["v_cache"])
+
+
+def test_tree_of_a_chain_equals_causal_verify():
+    spec, inp, q, kc, vc = _tree_inputs(31)
+    chain = np.tile((1 << (np.arange(spec.q_len) + 1)) - 1, spec.batch).astype(np.int32)
+    for window in (0, 11):
+        a = oracle.decode_paged_tree(q, kc, vc, inp["page_table"], inp["kv_lens"], chain, inp["sinks"], spec.q_len,
+                                     spec.scale, window)
+        b = oracle.decode_paged(q, kc, vc, inp["page_table"], inp["kv_lens"], inp["sinks"], spec.q_len, spec.scale,
+                                True, window)
+        np.testing.assert_allclose(a[0], b[0], atol=1e-13, rtol=0)
+        np.testing.assert_allclose(a[1], b[1], atol=1e-13, rtol=0)
+
+
+def test_tree_without_draft_bits_sees_the_prefix_only():
+    spec, inp, q, kc, vc = _tree_inputs(32)
+    none = np.zeros(spec.batch * spec.q_len, dtype=np.int32)
+    out, lse = oracle.decode_paged_tree(q, kc, vc, inp["page_table"], inp["kv_lens"], none, inp["sinks"],
+                                        spec.q_len, spec.scale)
+    for b, L in enumerate(inp["kv_lens"]):
+        pre = int(L) - spec.q_len
+        kb = _flat_gather(kc, inp["page_table"][b], L)[:pre]
+        vb = _flat_gather(vc, inp["page_table"][b], L)[:pre]
+        o2, l2 = oracle.attend(q[b * spec.q_len:(b + 1) * spec.q_len], kb, vb, inp["sinks"], spec.scale, False, 0)
+        np.testing.assert_allclose(out[b * spec.q_len:(b + 1) * spec.q_len], o2, atol=1e-13, rtol=0)
+        np.testing.assert_allclose(lse[b * spec.q_len:(b + 1) * spec.q_len], l2, atol=1e-13, rtol=0)
+
+
+def test_tree_verify_against_library_masked_attention():
+    spec, inp, q, kc, vc = _tree_inputs(33, q_len=8)
+    trees = make_tree_masks(spec)
+    out, lse = oracle.decode_paged_tree(q, kc, vc, inp["page_table"], inp["kv_lens"], trees, inp["sinks"],
+                                        spec.q_len, spec.scale)
+    G = spec.hq // spec.hkv
+    for b, L in enumerate(inp["kv_lens"]):
+        L = int(L)
+        rows = slice(b * spec.q_len, (b + 1) * spec.q_len)
+        # the mask written out from the tree's parent links, not from the oracle's helper
+        mask = np.ones((spec.q_len, L), dtype=bool)
+        mask[:, L - spec.q_len:] = False
+        for t in range(spec.q_len):
+            for i in range(spec.q_len):
+                if trees[b * spec.q_len + t] & (1 << i):
+                    mask[t, L - spec.q_len + i] = True
+        kb = _flat_gather(kc, inp["page_table"][b], L)
+        vb = _flat_gather(vc, inp["page_table"][b], L)
+        qt = torch.from_numpy(np.ascontiguousarray(q[rows].transpose(1, 0, 2)))
+        kt = torch.from_numpy(np.ascontiguousarray(kb.transpose(1, 0, 2))).repeat_interleave(G, 0)
+        vt = torch.from_numpy(np.ascontiguousarray(vb.transpose(1, 0, 2))).repeat_interleave(G, 0)
+        po = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask),
+                                                              scale=spec.scale).numpy().transpose(1, 0, 2)
+        s = spec.scale * torch.einsum("hqd,hkd->hqk", qt, kt).numpy()
+        pl = np.log(np.where(mask[None], np.exp(s), 0.0).sum(-1)).T
+        sig = 1.0 / (1.0 + np.exp(inp["sinks"][None, :].astype(np.float64) - pl))
+        np.testing.assert_allclose(out[rows], po * sig[..., None], atol=1e-12, rtol=0)
+        np.testing.assert_allclose(lse[rows], np.logaddexp(pl, inp["sinks"][None, :]), atol=1e-12, rtol=0)
+
+
+def test_tree_masks_are_ancestor_closed():
+    spec = CONFIGS["tree_verify"]
+    trees = make_tree_masks(spec, batch=50).reshape(50, spec.q_len)
+    for row in trees:
+        assert row[0] == 1
+        for i in range(1, spec.q_len):
+            assert row[i] & (1 << i) and row[i] < (1 << (i + 1))      # itself, no later node
+            parents = [j for j in range(i) if row[i] & (1 << j) and (row[i] & ~(1 << i)) == row[j]]
+            assert len(parents) == 1                                     # exactly one parent
 
 # ---------------------------------------------------------------------------------------
 # c-P9: a large sink takes the weight

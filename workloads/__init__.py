@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "VarlenSpec", "PagedSpec", "PagedPrefillSpec", "CONFIGS", "bf16_round_bits", "bf16_bits_to_f32",
-    "make_varlen", "make_paged", "make_paged_prefill", "scaled",
+    "make_varlen", "make_paged", "make_paged_prefill", "make_tree_masks", "scaled",
 ]
 
 
@@ -156,6 +156,10 @@ CONFIGS = {
     # Chunked prefill on the paged cache (the LLM prefill path of "Fast Embeddings on GPUs"):
     # 8 sequences each append a 2048-token chunk to 0..6144 cached tokens; 64/8 heads as
     # the prefill workload, 16-token pages.
+    # Verification of an 8-node draft tree per sequence (EAGLE-style drafts of "Accelerating Sonar
+    # through speculation"), on the verify workload's cache shape; one random tree per sequence.
+    "tree_verify": PagedSpec("tree_verify", batch=32, q_len=8, kv_len=(2048, 16384), hq=64, hkv=8,
+                             page_size=16, kv_chunk=2048, sink_std=2.0, seed=6),
     "chunked_prefill": PagedPrefillSpec("chunked_prefill", batch=8, q_len=(2048, 2048), ctx_len=(0, 6144),
                                         hq=64, hkv=8, page_size=16, sink_std=2.0, seed=5),
 }
@@ -273,3 +277,18 @@ def make_paged_prefill(spec: PagedPrefillSpec, q_lens: Optional[np.ndarray] = No
     return dict(q=q, cu_seqlens_q=cu, q_lens=ql, kv_lens=lens, k_cache=k_cache, v_cache=v_cache,
                 page_table=table, sinks=sinks, num_pages=pool,
                 max_q=int(ql.max()) if len(ql) else 0, max_kv_len=int(lens.max()) if len(lens) else 0)
+
+
+def make_tree_masks(spec: PagedSpec, batch: Optional[int] = None) -> np.ndarray:
+    """Random draft trees, one per sequence, as int32 bitmaps [batch * q_len]: node 0 is the
+    root, node i > 0 hangs under a parent drawn uniformly from nodes 0..i-1, and row i has the
+    bits of node i and of all its ancestors. Drawn from ``default_rng([seed, 1])``, a stream
+    apart from the paged inputs'."""
+    rng = np.random.default_rng([spec.seed, 1])
+    n = spec.batch if batch is None else batch
+    out = np.zeros(n * spec.q_len, dtype=np.int32)
+    for b in range(n):
+        for i in range(spec.q_len):
+            parent = int(rng.integers(0, i)) if i > 0 else -1
+            out[b * spec.q_len + i] = (1 << i) | (out[b * spec.q_len + parent] if parent >= 0 else 0)
+    return out
