@@ -19,7 +19,7 @@ from .build import LIB_LOAD_PATH as LIB_PATH
 
 __all__ = [
     "lib", "AttnSinkError", "attn_sink_prefill", "attn_sink_prefill_paged", "attn_sink_decode_paged",
-    "attn_sink_decode_paged_partials",
+    "attn_sink_decode_paged_partials", "attn_sink_decode_paged_tree",
     "attn_sink_decode_workspace_size",
     "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version", "decode_workspace_layout",
     "EXPORTED_SYMBOLS",
@@ -27,6 +27,7 @@ __all__ = [
 
 EXPORTED_SYMBOLS = (
     "attn_sink_prefill", "attn_sink_prefill_paged", "attn_sink_decode_paged", "attn_sink_decode_paged_partials",
+    "attn_sink_decode_paged_tree",
     "attn_sink_decode_workspace_size", "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version",
 )
 
@@ -45,6 +46,9 @@ lib.attn_sink_prefill.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _i32
 lib.attn_sink_prefill_paged.restype = ctypes.c_int
 lib.attn_sink_prefill_paged.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _fp, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _f32, _i32, _i32, _vp, _fp, _vp]
+lib.attn_sink_decode_paged_tree.restype = ctypes.c_int
+lib.attn_sink_decode_paged_tree.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _fp, _i32, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _fp, _vp]
 lib.attn_sink_decode_paged.restype = ctypes.c_int
 lib.attn_sink_decode_paged.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz, _vp, _fp, _vp]
@@ -279,6 +283,45 @@ def attn_sink_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                     _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
                                     _ptr(lse), _stream(stream))
     _raise(st, "attn_sink_decode_paged")
+    return out, lse
+
+
+def attn_sink_decode_paged_tree(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                page_table: torch.Tensor, kv_lens: torch.Tensor, tree_mask: torch.Tensor,
+                                sinks: Optional[torch.Tensor], q_len: int, max_kv_len: int,
+                                softmax_scale: Optional[float] = None, window: int = 0, kv_chunk: int = 512,
+                                workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                                lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """As attn_sink_decode_paged, with tree_mask int32 [batch*q_len] bitmaps (bit i of row t: draft token i
+    visible to draft token t) in place of the causal flag."""
+    batch, rows, hq, d, workspace = _decode_args(q, k_cache, v_cache, page_table, kv_lens, sinks, q_len, workspace,
+                                                 kv_chunk, max_kv_len)
+    dev = q.device
+    _check(tree_mask, "tree_mask", torch.int32, dev)
+    if tree_mask.numel() != rows:
+        raise ValueError(f"tree_mask must have batch * q_len = {rows} entries")
+    if out is not None:
+        _check(out, "out", torch.bfloat16, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, dev)
+        if lse.shape != (rows, hq):
+            raise ValueError(f"lse must be [{rows}, {hq}]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((rows, hq), dtype=torch.float32, device=dev)
+    num_pages, hkv, page_size = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    st = lib.attn_sink_decode_paged_tree(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), page_table.shape[1],
+                                         num_pages, _ptr(kv_lens), _ptr(tree_mask), _ptr(sinks), batch, q_len,
+                                         int(max_kv_len), hq, hkv, d, page_size, float(softmax_scale), int(window),
+                                         int(kv_chunk), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _ptr(out), _ptr(lse), _stream(stream))
+    _raise(st, "attn_sink_decode_paged_tree")
     return out, lse
 
 

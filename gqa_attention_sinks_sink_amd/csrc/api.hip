@@ -248,6 +248,7 @@ attn_sink_status decode_prepare(const void* q, const void* k_cache, const void* 
   p.causal = causal != 0;
   p.window = window > 0 ? window : 0;
   p.scale_log2 = softmax_scale * kLog2e;
+  p.tree_mask = nullptr;
   return ATTN_SINK_OK;
 }
 }  // namespace
@@ -261,13 +262,45 @@ attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, cons
                                         int32_t head_dim, int32_t page_size, float softmax_scale, int32_t causal,
                                         int32_t window, int32_t kv_chunk, void* workspace, size_t workspace_bytes,
                                         void* out, float* lse, void* stream) {
-  DecodeParams p;
+  DecodeParams p{};
   DecodeLayout lay;
   const attn_sink_status st = decode_prepare(q, k_cache, v_cache, page_table, max_pages_per_seq, num_pages, kv_lens,
                                              sinks, batch, q_len, max_kv_len, num_q_heads, num_kv_heads, head_dim,
                                              page_size, softmax_scale, causal, window, kv_chunk, workspace,
                                              workspace_bytes, out, true, &p, &lay);
   if (st != ATTN_SINK_OK || batch == 0) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_decode_split(p, (int)lay.chunks, s);
+  if (e != hipSuccess) return ATTN_SINK_ERR_HIP;
+
+  MergeParams mp;
+  mp.o_part = p.o_part;
+  mp.lse_part = p.lse_part;
+  mp.indptr = p.indptr;
+  mp.out = static_cast<uint16_t*>(out);
+  mp.lse = lse;
+  mp.num_partials = (int)lay.partials;
+  mp.rows = (int)lay.rows;
+  mp.hq = num_q_heads;
+  return hip_status(launch_merge(mp, s));
+}
+
+attn_sink_status attn_sink_decode_paged_tree(const void* q, const void* k_cache, const void* v_cache,
+                                             const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+                                             const int32_t* kv_lens, const int32_t* tree_mask, const float* sinks,
+                                             int32_t batch, int32_t q_len, int32_t max_kv_len, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                             float softmax_scale, int32_t window, int32_t kv_chunk, void* workspace,
+                                             size_t workspace_bytes, void* out, float* lse, void* stream) {
+  DecodeParams p{};
+  DecodeLayout lay;
+  const attn_sink_status st = decode_prepare(q, k_cache, v_cache, page_table, max_pages_per_seq, num_pages, kv_lens,
+                                             sinks, batch, q_len, max_kv_len, num_q_heads, num_kv_heads, head_dim,
+                                             page_size, softmax_scale, 1, window, kv_chunk, workspace,
+                                             workspace_bytes, out, true, &p, &lay);
+  if (st != ATTN_SINK_OK || batch == 0) return st;
+  if (tree_mask == nullptr) return ATTN_SINK_ERR_INVALID_ARG;
+  p.tree_mask = tree_mask;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = launch_decode_split(p, (int)lay.chunks, s);
   if (e != hipSuccess) return ATTN_SINK_ERR_HIP;
@@ -292,7 +325,7 @@ attn_sink_status attn_sink_decode_paged_partials(const void* q, const void* k_ca
                                                  int32_t page_size, float softmax_scale, int32_t causal,
                                                  int32_t window, int32_t kv_chunk, void* workspace,
                                                  size_t workspace_bytes, void* stream) {
-  DecodeParams p;
+  DecodeParams p{};
   DecodeLayout lay;
   const attn_sink_status st = decode_prepare(q, k_cache, v_cache, page_table, max_pages_per_seq, num_pages, kv_lens,
                                              sinks, batch, q_len, max_kv_len, num_q_heads, num_kv_heads, head_dim,

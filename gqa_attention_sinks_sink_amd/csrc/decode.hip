@@ -120,7 +120,7 @@ __device__ __forceinline__ void wait_lgkm0() {
 
 }  // namespace
 
-template <int NT>
+template <int NT, bool TREE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeParams p) {
   constexpr int S = DecodeRing<NT>::value;
@@ -306,11 +306,30 @@ void decode_split_kernel(DecodeParams p) {
     int hi_min = 0x7fffffff, lo_max = -0x7fffffff;
     float m[NT], lsum[NT];
     f32x4 o[NT][4];
+    // Draft tree: each column's bitmap of visible draft tokens (the last q_len keys); the q_len
+    // bitmaps of the sequence come in through scalar loads.
+    const int blk0 = L - p.q_len;
+    int tbits[NT];
+    if constexpr (TREE) {
+      const int32_t* tb = p.tree_mask + (size_t)b * p.q_len;
+      int sv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = tb[min(i, p.q_len - 1)];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = nt * 16 + col_lo;
+        const int t = col < R ? col / G : 0;
+        int v = sv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) v = (t == i) ? sv[i] : v;
+        tbits[nt] = v;
+      }
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int col = nt * 16 + col_lo;
       const int pos = L - p.q_len + col / G;
-      vis_hi[nt] = p.causal ? min(cur.chunk_hi, pos + 1) : cur.chunk_hi;
+      vis_hi[nt] = (p.causal && !TREE) ? min(cur.chunk_hi, pos + 1) : cur.chunk_hi;
       vis_lo[nt] = (p.window > 0) ? max(cur.chunk_lo, pos - p.window + 1) : cur.chunk_lo;
       if (vis_hi[nt] < vis_lo[nt]) vis_hi[nt] = vis_lo[nt];
       if (col < R) {
@@ -374,14 +393,22 @@ void decode_split_kernel(DecodeParams p) {
       // ---- masks (only on groups that straddle a bound) + online softmax with a lazy max:
       // m moves only when some score exceeds it by more than kLazyMax (log2 units); every term
       // of a column always uses that column's current m, so the softmax is unchanged.
-      if (!(key0 + kGroupKeys <= hi_min && key0 >= lo_max)) {
+      if (!(key0 + kGroupKeys <= hi_min && key0 >= lo_max) || (TREE && key0 + kGroupKeys > blk0)) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const unsigned span = (unsigned)(vis_hi[nt] - vis_lo[nt]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = key0 + 4 * grp + i;
-            sc[nt][i] = ((unsigned)(key - vis_lo[nt]) < span) ? sc[nt][i] : kNegInf;
+            bool vis = (unsigned)(key - vis_lo[nt]) < span;
+            if constexpr (TREE) {
+              // Draft keys follow the column's bitmap; prefix keys (dk wraps past 31) are kept.
+              // Branch-free, with the shift amount kept in range.
+              const unsigned dk = (unsigned)(key - blk0);
+              const unsigned bit = ((unsigned)tbits[nt] >> (dk & 31u)) & 1u;
+              vis = vis && (dk > 31u || bit != 0u);
+            }
+            sc[nt][i] = vis ? sc[nt][i] : kNegInf;
           }
         }
       }
@@ -516,17 +543,17 @@ void decode_split_kernel(DecodeParams p) {
 }
 
 namespace {
-template <int NT>
+template <int NT, bool TREE>
 int resident_blocks_per_cu() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<NT>, kThreads, 0) != hipSuccess || n < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<NT, TREE>, kThreads, 0) != hipSuccess || n < 1)
     n = 1;
   return n;
 }
 
 struct DeviceShape {
   int cus = 0;
-  int blocks_per_cu[5] = {0, 0, 0, 0, 0};
+  int blocks_per_cu[2][5] = {{0, 0, 0, 0, 0}, {0, 0, 0, 0, 0}};  // [tree][column tiles]
 };
 
 // Per-device launch shape, computed once per device from host-side queries.
@@ -538,10 +565,14 @@ const DeviceShape& device_shape() {
   if (s.cus == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    s.blocks_per_cu[1] = resident_blocks_per_cu<1>();
-    s.blocks_per_cu[2] = resident_blocks_per_cu<2>();
-    s.blocks_per_cu[3] = resident_blocks_per_cu<3>();
-    s.blocks_per_cu[4] = resident_blocks_per_cu<4>();
+    s.blocks_per_cu[0][1] = resident_blocks_per_cu<1, false>();
+    s.blocks_per_cu[0][2] = resident_blocks_per_cu<2, false>();
+    s.blocks_per_cu[0][3] = resident_blocks_per_cu<3, false>();
+    s.blocks_per_cu[0][4] = resident_blocks_per_cu<4, false>();
+    s.blocks_per_cu[1][1] = resident_blocks_per_cu<1, true>();
+    s.blocks_per_cu[1][2] = resident_blocks_per_cu<2, true>();
+    s.blocks_per_cu[1][3] = resident_blocks_per_cu<3, true>();
+    s.blocks_per_cu[1][4] = resident_blocks_per_cu<4, true>();
     s.cus = cus;
   }
   return s;
@@ -553,17 +584,27 @@ hipError_t launch_decode_split(const DecodeParams& p, int max_chunks, hipStream_
   const int nt = (R + 15) / 16;
   if (nt < 1 || nt > 4) return hipErrorInvalidValue;
   const DeviceShape& ds = device_shape();
+  const bool tree = p.tree_mask != nullptr;
   // Persistent grid: enough workgroups to fill every CU, never more than the item bound.
   const long item_bound = (long)max_chunks * p.batch * p.hkv;
-  long blocks = (long)ds.cus * ds.blocks_per_cu[nt];
+  long blocks = (long)ds.cus * ds.blocks_per_cu[tree ? 1 : 0][nt];
   if (blocks > item_bound) blocks = item_bound;
   if (blocks < 1) blocks = 1;
   dim3 grid((unsigned)blocks), block(kThreads);
-  switch (nt) {
-    case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL(decode_split_kernel<3>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(decode_split_kernel<4>, grid, block, 0, stream, p); break;
+  if (tree) {
+    switch (nt) {
+      case 1: hipLaunchKernelGGL((decode_split_kernel<1, true>), grid, block, 0, stream, p); break;
+      case 2: hipLaunchKernelGGL((decode_split_kernel<2, true>), grid, block, 0, stream, p); break;
+      case 3: hipLaunchKernelGGL((decode_split_kernel<3, true>), grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL((decode_split_kernel<4, true>), grid, block, 0, stream, p); break;
+    }
+  } else {
+    switch (nt) {
+      case 1: hipLaunchKernelGGL((decode_split_kernel<1, false>), grid, block, 0, stream, p); break;
+      case 2: hipLaunchKernelGGL((decode_split_kernel<2, false>), grid, block, 0, stream, p); break;
+      case 3: hipLaunchKernelGGL((decode_split_kernel<3, false>), grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL((decode_split_kernel<4, false>), grid, block, 0, stream, p); break;
+    }
   }
   return hipGetLastError();
 }

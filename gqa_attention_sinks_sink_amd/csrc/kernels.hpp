@@ -21,6 +21,9 @@ struct DecodeParams {
   int page_size, page_shift, max_pages, num_pages;
   int kv_chunk, causal, window;
   float scale_log2;  // softmax_scale * log2(e)
+  // Draft-tree verification when non-null: [batch * q_len] bitmaps, bit i of row b * q_len + t
+  // = draft token i visible to token t (the prefix is always visible; causal is not used).
+  const int32_t* tree_mask;
 };
 
 struct MergeParams {

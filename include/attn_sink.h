@@ -180,6 +180,30 @@ attn_sink_status attn_sink_decode_paged(
     void* out, float* lse, void* stream);
 
 /*
+ * Verification of a draft tree in one step ("Accelerating Sonar through speculation", EAGLE
+ * section: tree-shaped drafts need a custom attention mask, which a full-sequence mask made
+ * costly). The mask is a bitmap per draft row: the q_len draft tokens are the last q_len of
+ * each sequence's kv_lens[b] tokens, and row b * q_len + t sees every earlier (prefix) token
+ * plus the draft tokens i whose bit i is set in tree_mask[b * q_len + t] (set bits >= q_len
+ * are ignored). A window > 0 also bounds every key by position (p - j < window).
+ *
+ *   tree_mask    int32 [batch * q_len] on the device (a chain, bits 0..t for row t, is the
+ *                causal verify of attn_sink_decode_paged).
+ * Every other argument, constraint and error code as for attn_sink_decode_paged (there is no
+ * causal flag: the bitmaps decide inside the draft block); tree_mask NULL is
+ * ATTN_SINK_ERR_INVALID_ARG. Enqueues two kernels (split-KV chunks, then the merge).
+ */
+attn_sink_status attn_sink_decode_paged_tree(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    const int32_t* kv_lens, const int32_t* tree_mask, const float* sinks,
+    int32_t batch, int32_t q_len, int32_t max_kv_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    float softmax_scale, int32_t window, int32_t kv_chunk,
+    void* workspace, size_t workspace_bytes,
+    void* out, float* lse, void* stream);
+
+/*
  * The split-KV pass of attn_sink_decode_paged alone: writes the plan and the chunk partials
  * into the workspace (layout above) and does not merge them. Arguments, constraints and
  * error codes as for attn_sink_decode_paged, without out and lse. For callers that merge

@@ -142,6 +142,30 @@ def _decode(amd, **kw):
                                           a["chunk"], a["ws"], a["ws_bytes"], a["out"], a["lse"], a["stream"])
 
 
+def _decode_tree(amd, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, max_pages=512, num_pages=100, kv_lens=FAKE, tree=FAKE, sinks=None,
+             batch=4, q_len=8, max_kv=8192, hq=64, hkv=8, d=64, page=16, scale=0.125, window=0, chunk=512,
+             ws=FAKE, ws_bytes=1 << 40, out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return amd.lib.attn_sink_decode_paged_tree(a["q"], a["k"], a["v"], a["table"], a["max_pages"], a["num_pages"],
+                                               a["kv_lens"], a["tree"], a["sinks"], a["batch"], a["q_len"],
+                                               a["max_kv"], a["hq"], a["hkv"], a["d"], a["page"], a["scale"],
+                                               a["window"], a["chunk"], a["ws"], a["ws_bytes"], a["out"], a["lse"],
+                                               a["stream"])
+
+
+def test_decode_tree_argument_errors(amd):
+    assert _decode_tree(amd, tree=None) == INVALID
+    assert _decode_tree(amd, d=128) == UNSUPPORTED
+    assert _decode_tree(amd, q_len=9) == UNSUPPORTED
+    assert _decode_tree(amd, hq=72, hkv=8) == UNSUPPORTED      # 8 x 9 columns
+    assert _decode_tree(amd, page=8) == UNSUPPORTED
+    assert _decode_tree(amd, chunk=100) == UNSUPPORTED
+    assert _decode_tree(amd, scale=-1.0) == INVALID
+    assert _decode_tree(amd, out=None) == INVALID
+    assert _decode_tree(amd, ws_bytes=16) == WS_SMALL
+    assert _decode_tree(amd, batch=0, tree=None) == OK        # nothing to do
+
 def test_decode_argument_errors(amd):
     assert _decode(amd, d=128) == UNSUPPORTED
     assert _decode(amd, q_len=9) == UNSUPPORTED

@@ -11,7 +11,8 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
-from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_paged_prefill, make_varlen, scaled  # noqa: E402
+from workloads import (CONFIGS, bf16_bits_to_f32, make_paged, make_paged_prefill, make_tree_masks,  # noqa: E402
+                       make_varlen, scaled)
 
 pytestmark = pytest.mark.gpu
 
@@ -448,6 +449,67 @@ def test_decode_full_size(amd, name):
     ro, rl = oracle_decode(inp, spec, seqs=seqs)
     assert_close(out, lse, ro, rl, name)
 
+
+# -------------------------------------------------------------------------------------------
+# draft-tree verification
+# -------------------------------------------------------------------------------------------
+def run_tree(amd, d, inp, spec, trees, chunk=None, window=None):
+    out, lse = amd.attn_sink_decode_paged_tree(d["q"], d["k"], d["v"], d["table"], d["lens"],
+                                               torch.from_numpy(trees).to(DEV), d["sinks"], spec.q_len,
+                                               inp["max_kv_len"], spec.scale, spec.window if window is None else window,
+                                               spec.kv_chunk if chunk is None else chunk)
+    torch.cuda.synchronize()
+    return out_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_tree(inp, spec, trees, seqs=None, window=None):
+    return oracle.decode_paged_tree(f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"]), inp["page_table"],
+                                    inp["kv_lens"], trees, inp["sinks"], spec.q_len, spec.scale,
+                                    spec.window if window is None else window, seqs=seqs)
+
+
+@pytest.mark.parametrize("q_len,hq,hkv,chunk,window", [(8, 64, 8, 512, 0), (8, 16, 2, 64, 0), (5, 16, 2, 2048, 0),
+                                                       (3, 8, 1, 128, 0), (8, 8, 8, 512, 40), (2, 32, 8, 0, 0)])
+def test_tree_verify_small(amd, q_len, hq, hkv, chunk, window):
+    spec = scaled(CONFIGS["tree_verify"], batch=5, q_len=q_len, kv_len=(q_len, 1500), hq=hq, hkv=hkv, kv_chunk=chunk,
+                  window=window, seed=90 + q_len + hq)
+    inp = make_paged(spec)
+    trees = make_tree_masks(spec)
+    out, lse = run_tree(amd, dev_paged(inp), inp, spec, trees)
+    ro, rl = oracle_tree(inp, spec, trees)
+    assert_close(out, lse, ro, rl, f"tree q_len={q_len} hq={hq} hkv={hkv} chunk={chunk} window={window}")
+
+
+def test_tree_chain_is_bit_identical_to_causal_verify(amd):
+    spec = scaled(CONFIGS["verify"], batch=6, kv_len=(5, 3000), hq=64, hkv=8, kv_chunk=512, seed=97)
+    inp = make_paged(spec)
+    d = dev_paged(inp)
+    chain = np.tile((1 << (np.arange(spec.q_len) + 1)) - 1, spec.batch).astype(np.int32)
+    a = run_decode(amd, d, inp, spec)
+    b = run_tree(amd, d, inp, spec, chain)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_tree_edge_bitmaps(amd):
+    # empty bitmaps (prefix only), all bits (every draft token), bits past q_len (ignored),
+    # sequences no longer than the draft block
+    spec = scaled(CONFIGS["tree_verify"], batch=4, q_len=6, kv_len=(6, 700), hq=16, hkv=2, kv_chunk=256, seed=98)
+    inp = make_paged(spec, kv_lens=[6, 7, 300, 700])
+    q = spec.q_len
+    for trees in (np.zeros(4 * q, np.int32), np.full(4 * q, (1 << q) - 1, np.int32),
+                  (make_tree_masks(spec) | np.int32(-(1 << q))).astype(np.int32)):
+        out, lse = run_tree(amd, dev_paged(inp), inp, spec, trees)
+        ro, rl = oracle_tree(inp, spec, trees & ((1 << q) - 1))
+        assert_close(out, lse, ro, rl, "tree edge bitmaps")
+
+
+def test_tree_verify_full_size_sampled(amd):
+    spec = CONFIGS["tree_verify"]
+    inp = make_paged(spec)
+    trees = make_tree_masks(spec)
+    out, lse = run_tree(amd, dev_paged(inp), inp, spec, trees)
+    ro, rl = oracle_tree(inp, spec, trees, seqs=[0, 1, 13, 31])
+    assert_close(out, lse, ro, rl, "tree_verify")
 
 # -------------------------------------------------------------------------------------------
 # graph capture: launches depend on host scalars only, so calls can be captured and replayed
