@@ -7,7 +7,8 @@ order, 512-token chunks merged by log-sum-exp). One step = one attn_sink_decode_
 
 Other workloads (--workload): causal_prefill, window_prefill, verify, embed (two passes:
 sinks disabled, then N(0,1) sinks), chunked_prefill (2048-token chunks appended to paged
-caches of 0..6144 tokens), tiny_causal.
+caches of 0..6144 tokens), tree_verify (8-node draft trees per sequence, one-step
+verification), tiny_causal.
 
 Prints ONE JSON line. ``value`` is the algorithmic rate of the whole step (GB/s for the
 memory-bound paths, TFLOP/s for prefill); ``roofline`` describes the dominant kernel, timed
@@ -28,7 +29,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import CONFIGS, bf16_bits_to_f32, make_paged, make_paged_prefill, make_varlen  # noqa: E402
+from workloads import (CONFIGS, bf16_bits_to_f32, make_paged, make_paged_prefill, make_tree_masks,  # noqa: E402
+                       make_varlen)
 
 METRIC = "sink-attn decode HBM GB/s (% peak); prefill TFLOP/s (% bf16 MFMA peak)"
 HBM_PEAK_GBS = 8000.0
@@ -45,8 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="paged_decode",
-                    choices=["paged_decode", "verify", "causal_prefill", "window_prefill", "embed", "chunked_prefill",
-                             "tiny_causal"])
+                    choices=["paged_decode", "verify", "tree_verify", "causal_prefill", "window_prefill", "embed",
+                             "chunked_prefill", "tiny_causal"])
     ap.add_argument("--kv-chunk", type=int, default=None,
                     help="split-KV chunk length for the paged workloads (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU oracle sample (wall seconds)")
@@ -110,7 +112,7 @@ def prefill_kernel_name(spec, max_seqlen):
 
 
 def dominant_kernel(name):
-    if name in ("paged_decode", "verify"):
+    if name in ("paged_decode", "verify", "tree_verify"):
         return "decode_split_kernel"
     if name == "chunked_prefill":
         spec = CONFIGS[name]
@@ -205,7 +207,7 @@ def cold_time(torch, fn, steps, scratch):
 # ------------------------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample)
 # ------------------------------------------------------------------------------------------
-def cpu_baseline_paged(inp, spec, seconds, bytes_per_seq):
+def cpu_baseline_paged(inp, spec, seconds, bytes_per_seq, trees=None):
     import oracle
     from threadpoolctl import threadpool_limits
     f64 = lambda b: bf16_bits_to_f32(b).astype(np.float64)
@@ -221,9 +223,13 @@ def cpu_baseline_paged(inp, spec, seconds, bytes_per_seq):
             sub_k = f64(kc[pages])
             sub_v = f64(vc[pages])
             table = np.arange(len(pages), dtype=np.int32)[None, :]
-            oracle.decode_paged(q[b * spec.q_len:(b + 1) * spec.q_len], sub_k, sub_v, table,
-                                np.array([L], dtype=np.int32), inp["sinks"], spec.q_len, spec.scale, spec.causal,
-                                spec.window)
+            rows = slice(b * spec.q_len, (b + 1) * spec.q_len)
+            if trees is None:
+                oracle.decode_paged(q[rows], sub_k, sub_v, table, np.array([L], dtype=np.int32), inp["sinks"],
+                                    spec.q_len, spec.scale, spec.causal, spec.window)
+            else:
+                oracle.decode_paged_tree(q[rows], sub_k, sub_v, table, np.array([L], dtype=np.int32), trees[rows],
+                                         inp["sinks"], spec.q_len, spec.scale, spec.window)
             done_bytes += bytes_per_seq[b]
             n += 1
     dt = time.perf_counter() - t0
@@ -280,25 +286,38 @@ def bench_paged(args, torch, amd, name):
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty((B * ql, hq), dtype=torch.float32, device=dev)
+    tree = name == "tree_verify"
+    trees = make_tree_masks(spec) if tree else None
+    trees_d = torch.from_numpy(trees).to(dev) if tree else None
 
     def step():
-        amd.attn_sink_decode_paged(q, kc, vc, table, lens, sinks, ql, inp["max_kv_len"], spec.scale, spec.causal,
-                                   spec.window, spec.kv_chunk, workspace=ws, out=out, lse=lse)
+        if tree:
+            amd.attn_sink_decode_paged_tree(q, kc, vc, table, lens, trees_d, sinks, ql, inp["max_kv_len"], spec.scale,
+                                            spec.window, spec.kv_chunk, workspace=ws, out=out, lse=lse)
+        else:
+            amd.attn_sink_decode_paged(q, kc, vc, table, lens, sinks, ql, inp["max_kv_len"], spec.scale, spec.causal,
+                                       spec.window, spec.kv_chunk, workspace=ws, out=out, lse=lse)
 
     L = inp["kv_lens"].astype(np.int64)
     kv_bytes_seq = L * hkv * 64 * 2 * 2
     pages_seq = (L + spec.page_size - 1) // spec.page_size
     q_bytes = B * ql * hq * 64 * 2
-    algo_bytes = int(kv_bytes_seq.sum() + q_bytes * 2 + B * ql * hq * 4 + pages_seq.sum() * 4 + B * 4 + hq * 4)
-    kernel_bytes = int(kv_bytes_seq.sum() + q_bytes + pages_seq.sum() * 4)   # split-KV kernel, per launch
-    flops = int((L * hkv).sum() * (hq // hkv) * ql * 4 * 64)
+    tree_bytes = B * ql * 4 if tree else 0
+    algo_bytes = int(kv_bytes_seq.sum() + q_bytes * 2 + B * ql * hq * 4 + pages_seq.sum() * 4 + B * 4 + hq * 4
+                     + tree_bytes)
+    kernel_bytes = int(kv_bytes_seq.sum() + q_bytes + pages_seq.sum() * 4 + tree_bytes)   # split-KV kernel, per launch
+    if tree:   # visible keys per row: the prefix plus the row's draft bits
+        bits = np.array([bin(int(x) & ((1 << ql) - 1)).count("1") for x in trees], dtype=np.int64).reshape(B, ql)
+        flops = int(((L[:, None] - ql + bits) * hq).sum() * 4 * 64)
+    else:
+        flops = int((L * hkv).sum() * (hq // hkv) * ql * 4 * 64)
 
     ms = time_calls(torch, step, args.steps, args.warmup)
     # the split-KV kernel alone (the split-only entry point: the same kernel, no merge)
     def split_only():
         amd.attn_sink_decode_paged_partials(q, kc, vc, table, lens, sinks, ql, inp["max_kv_len"], spec.scale,
                                             spec.causal, spec.window, spec.kv_chunk, workspace=ws)
-    split_ms = time_calls(torch, split_only, args.steps, args.warmup)
+    split_ms = None if tree else time_calls(torch, split_only, args.steps, args.warmup)
     # merge kernel alone on the same partials
     lay = amd.decode_workspace_layout(B, ql, inp["max_kv_len"], hq, spec.kv_chunk, spec.page_size)
     n_p = lay["partials"]
@@ -308,6 +327,8 @@ def bench_paged(args, torch, amd, name):
     out2 = torch.empty_like(out)
     merge_ms = time_calls(torch, lambda: amd.attn_sink_merge_partials(o_p, l_p, indptr, out=out2, return_lse=False),
                           args.steps, args.warmup)
+    if split_ms is None:   # tree mode has no split-only entry point: the call minus its merge
+        split_ms = ms - merge_ms
     cold_ms = None
     if not args.no_cold:
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -320,7 +341,8 @@ def bench_paged(args, torch, amd, name):
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{name}: {B} seqs x q_len {ql}, kv {spec.kv_len[0]}..{spec.kv_len[1]} "
+        "config": {"workload": f"{name}: {B} seqs x q_len {ql}{' (8-node random draft trees)' if tree else ''}, "
+                               f"kv {spec.kv_len[0]}..{spec.kv_len[1]} "
                                f"(sum {int(L.sum())}), {hq}/{hkv} heads, d 64, {spec.page_size}-token pages, "
                                f"{spec.kv_chunk}-token chunks, sinks N(0,{spec.sink_std}^2)",
                    "algorithmic_bytes": algo_bytes, "algorithmic_flops": flops},
@@ -334,7 +356,7 @@ def bench_paged(args, torch, amd, name):
         res["cold_l2_mall_ms_per_step"] = round(cold_ms, 5)
         res["cold_value"] = round(algo_bytes / (cold_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
-        v, n, dt = cpu_baseline_paged(inp, spec, args.cpu_seconds, kv_bytes_seq)
+        v, n, dt = cpu_baseline_paged(inp, spec, args.cpu_seconds, kv_bytes_seq, trees)
         res["cpu_baseline"] = {"value": round(v, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                                "sample": f"{n} sequences of this batch (cycled from sequence 0), {dt:.1f} s wall, "
                                          f"fp64 NumPy, BLAS limited to 1 thread"}
@@ -512,7 +534,7 @@ def bench_chunked(args, torch, amd, name):
 def main():
     args = parse()
     if args.record_traffic:
-        kind = "decode" if args.workload in ("paged_decode", "verify") else "prefill"
+        kind = "decode" if args.workload in ("paged_decode", "verify", "tree_verify") else "prefill"
         record_traffic(args.workload, kind, *args.record_traffic)
         return
     if args.gpus != 1:
@@ -531,7 +553,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30}))
         return
-    if args.workload in ("paged_decode", "verify"):
+    if args.workload in ("paged_decode", "verify", "tree_verify"):
         res = bench_paged(args, torch, amd, args.workload)
     elif args.workload == "chunked_prefill":
         res = bench_chunked(args, torch, amd, args.workload)
