@@ -11,7 +11,9 @@ scaled Q.K scores; the sink has no value vector. ``attention.attend`` writes out
 definition directly (one softmax over [scores, sink]). ``attention.online_partials``
 follows the streaming form the same section describes (running max seeded with the
 head's sink, scale initialised to 1, sink only in the first KV chunk) and
-``attention.merge`` combines split-KV partials by log-sum-exp.
+``attention.merge`` combines split-KV partials by log-sum-exp. ``rope`` holds the step
+before attention for new tokens: YaRN rotary encoding (named by the same page) and the
+write of the new K/V into the paged cache.
 
 Every function is pinned by tests under ``tests/`` that do not go through the
 oracle's own formulas (library attention with the sink disabled, closed forms,
@@ -25,3 +27,4 @@ from .attention import (  # noqa: F401
     tree_visible, decode_paged_tree,
     online_partials, split_decode, merge, plan_chunks,
 )
+from .rope import yarn_frequencies, rotate, rope_append  # noqa: F401
