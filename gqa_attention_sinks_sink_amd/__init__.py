@@ -11,7 +11,7 @@ __version__ = "0.1.0"
 
 _BINDING_NAMES = (
     "AttnSinkError", "EXPORTED_SYMBOLS", "attn_sink_decode_paged", "attn_sink_decode_paged_partials",
-    "attn_sink_prefill_paged", "attn_sink_decode_paged_tree",
+    "attn_sink_prefill_paged", "attn_sink_decode_paged_tree", "attn_sink_rope_append",
     "attn_sink_decode_workspace_size",
     "attn_sink_merge_partials", "attn_sink_prefill", "attn_sink_status_string", "attn_sink_version",
     "decode_workspace_layout", "lib",

@@ -19,7 +19,7 @@ from .build import LIB_LOAD_PATH as LIB_PATH
 
 __all__ = [
     "lib", "AttnSinkError", "attn_sink_prefill", "attn_sink_prefill_paged", "attn_sink_decode_paged",
-    "attn_sink_decode_paged_partials", "attn_sink_decode_paged_tree",
+    "attn_sink_decode_paged_partials", "attn_sink_decode_paged_tree", "attn_sink_rope_append",
     "attn_sink_decode_workspace_size",
     "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version", "decode_workspace_layout",
     "EXPORTED_SYMBOLS",
@@ -27,7 +27,7 @@ __all__ = [
 
 EXPORTED_SYMBOLS = (
     "attn_sink_prefill", "attn_sink_prefill_paged", "attn_sink_decode_paged", "attn_sink_decode_paged_partials",
-    "attn_sink_decode_paged_tree",
+    "attn_sink_decode_paged_tree", "attn_sink_rope_append",
     "attn_sink_decode_workspace_size", "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version",
 )
 
@@ -49,6 +49,9 @@ lib.attn_sink_prefill_paged.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp
 lib.attn_sink_decode_paged_tree.restype = ctypes.c_int
 lib.attn_sink_decode_paged_tree.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _fp, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _fp, _vp]
+lib.attn_sink_rope_append.restype = ctypes.c_int
+lib.attn_sink_rope_append.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _f32, _f32, _i32, _f32, _f32, _vp, _vp]
 lib.attn_sink_decode_paged.restype = ctypes.c_int
 lib.attn_sink_decode_paged.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz, _vp, _fp, _vp]
@@ -197,6 +200,43 @@ def attn_sink_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
                                      int(bool(causal)), int(window), _ptr(out), _ptr(lse), _stream(stream))
     _raise(st, "attn_sink_prefill_paged")
     return out, lse
+
+
+def attn_sink_rope_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                          kv_lens: torch.Tensor, page_table: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          max_seqlen_q: int, max_kv_len: int, rope_theta: float, yarn_factor: float = 1.0,
+                          yarn_original_len: int = 0, yarn_alpha: float = 1.0, yarn_beta: float = 32.0,
+                          q_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q [T, hq, 64], k/v [T, hkv, 64] bf16 (new tokens); caches [pages, hkv, page_size, 64] bf16, updated in
+    place; cu_seqlens_q int32 [batch+1]; kv_lens int32 [batch] (new tokens included). Returns the rotated q."""
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check(t, n, torch.bfloat16, dev)
+    for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (kv_lens, "kv_lens"), (page_table, "page_table")):
+        _check(t, n, torch.int32, dev)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] or k_cache.dim() != 4 or \
+            v_cache.shape != k_cache.shape or k_cache.shape[1] != k.shape[1] or k_cache.shape[3] != q.shape[2]:
+        raise ValueError(f"expected q [T, hq, d], k/v [T, hkv, d] and caches [pages, hkv, page_size, d]; got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}, {tuple(k_cache.shape)}")
+    total_q, hq, d = q.shape
+    hkv = k.shape[1]
+    batch = cu_seqlens_q.numel() - 1
+    if kv_lens.numel() != batch or page_table.dim() != 2 or page_table.shape[0] != batch:
+        raise ValueError("kv_lens must be [batch] and page_table [batch, max_pages] with batch = len(cu_seqlens_q) - 1")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    else:
+        _check(q_out, "q_out", torch.bfloat16, dev)
+        if q_out.shape != q.shape:
+            raise ValueError("q_out must have the shape of q")
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[2]
+    st = lib.attn_sink_rope_append(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(kv_lens), _ptr(page_table),
+                                   page_table.shape[1], num_pages, _ptr(k_cache), _ptr(v_cache), batch, total_q,
+                                   int(max_seqlen_q), int(max_kv_len), hq, hkv, d, page_size, float(rope_theta),
+                                   float(yarn_factor), int(yarn_original_len), float(yarn_alpha), float(yarn_beta),
+                                   _ptr(q_out), _stream(stream))
+    _raise(st, "attn_sink_rope_append")
+    return q_out
 
 
 def attn_sink_decode_workspace_size(batch: int, q_len: int, max_kv_len: int, num_q_heads: int, head_dim: int,

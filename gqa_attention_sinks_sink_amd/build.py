@@ -20,7 +20,7 @@ LIB_NAME = "libattnsink.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 # Developer override: load a library built elsewhere (e.g. an experimental variant).
 LIB_LOAD_PATH = os.environ.get("ATTN_SINK_LIB", LIB_PATH)
-SOURCES = ["api.hip", "prefill.hip", "decode.hip", "merge.hip"]
+SOURCES = ["api.hip", "prefill.hip", "decode.hip", "merge.hip", "rope.hip"]
 ARCH = "gfx950"
 
 

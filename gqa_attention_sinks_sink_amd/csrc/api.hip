@@ -1,6 +1,7 @@
 // C ABI of libattnsink.so: argument validation, workspace layout and kernel launches.
 // Every check runs on the host before anything is enqueued; nothing here allocates,
 // frees or synchronises.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstddef>
@@ -175,6 +176,67 @@ attn_sink_status attn_sink_prefill_paged(const void* q, const void* k_cache, con
   p.page_size = page_size;
   p.page_shift = ilog2(page_size);
   return hip_status(launch_prefill(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+attn_sink_status attn_sink_rope_append(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                                       const int32_t* kv_lens, const int32_t* page_table, int32_t max_pages_per_seq,
+                                       int32_t num_pages, void* k_cache, void* v_cache, int32_t batch, int32_t total_q,
+                                       int32_t max_seqlen_q, int32_t max_kv_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size, float rope_theta,
+                                       float yarn_factor, int32_t yarn_original_len, float yarn_alpha,
+                                       float yarn_beta, void* q_out, void* stream) {
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_kv_len < 0 || max_pages_per_seq < 1 || num_pages < 1)
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!(std::isfinite(rope_theta) && rope_theta > 1.f) || !(std::isfinite(yarn_factor) && yarn_factor > 0.f))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (yarn_factor > 1.f && !(yarn_original_len > 0 && std::isfinite(yarn_alpha) && std::isfinite(yarn_beta) &&
+                             yarn_alpha < yarn_beta))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kSupportedHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size < 16 || page_size > 256) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch > kMaxGridY) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr || kv_lens == nullptr ||
+      page_table == nullptr || k_cache == nullptr || v_cache == nullptr || q_out == nullptr)
+    return ATTN_SINK_ERR_INVALID_ARG;
+
+  RopeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.cu_q = cu_seqlens_q;
+  p.kv_lens = kv_lens;
+  p.page_table = page_table;
+  p.k_cache = static_cast<uint16_t*>(k_cache);
+  p.v_cache = static_cast<uint16_t*>(v_cache);
+  p.q_out = static_cast<uint16_t*>(q_out);
+  p.batch = batch;
+  p.total_q = total_q;
+  p.max_q = max_seqlen_q;
+  p.max_kv = max_kv_len;
+  p.hq = num_q_heads;
+  p.hkv = num_kv_heads;
+  p.max_pages = max_pages_per_seq;
+  p.num_pages = num_pages;
+  p.page_size = page_size;
+  p.page_shift = ilog2(page_size);
+  // YaRN: base frequencies theta^(-2i/d); with factor s > 1, a ramp over the turns r_i each
+  // pair makes in the original context keeps fast pairs (r >= beta), divides slow ones
+  // (r <= alpha) by s and blends in between; the temperature 0.1 ln s + 1 scales cos and sin.
+  const double pi2 = 6.283185307179586;
+  for (int i = 0; i < kSupportedHeadDim / 2; ++i) {
+    const double f = std::pow((double)rope_theta, -2.0 * i / kSupportedHeadDim);
+    double fi = f;
+    if (yarn_factor > 1.f) {
+      const double r = (double)yarn_original_len * f / pi2;
+      const double g = std::min(1.0, std::max(0.0, (r - yarn_alpha) / ((double)yarn_beta - yarn_alpha)));
+      fi = g * f + (1.0 - g) * f / yarn_factor;
+    }
+    p.freqs[i] = fi;
+  }
+  p.mscale = yarn_factor > 1.f ? (float)(0.1 * std::log((double)yarn_factor) + 1.0) : 1.f;
+  return hip_status(launch_rope_append(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t attn_sink_decode_workspace_size(int32_t batch, int32_t q_len, int32_t max_kv_len, int32_t num_q_heads,

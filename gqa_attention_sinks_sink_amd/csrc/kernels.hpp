@@ -57,7 +57,25 @@ struct PrefillParams {
   int max_pages, num_pages, page_size, page_shift;
 };
 
+// YaRN rotary encoding of new tokens and their append into the paged cache.
+struct RopeParams {
+  const uint16_t* q;  // bf16 [total_q, hq, 64]: the new tokens
+  const uint16_t* k;  // bf16 [total_q, hkv, 64]
+  const uint16_t* v;
+  const int32_t* cu_q;        // [batch + 1]
+  const int32_t* kv_lens;     // [batch], the new tokens included
+  const int32_t* page_table;  // [batch, max_pages]
+  uint16_t* k_cache;          // bf16 [num_pages, hkv, page_size, 64]
+  uint16_t* v_cache;
+  uint16_t* q_out;            // bf16 [total_q, hq, 64] (may be q)
+  int batch, total_q, max_q, max_kv, hq, hkv;
+  int max_pages, num_pages, page_size, page_shift;
+  float mscale;       // attention temperature factor applied to cos and sin
+  double freqs[32];   // angular frequency of pair (i, i + 32)
+};
+
 hipError_t launch_decode_split(const DecodeParams& p, int max_chunks, hipStream_t stream);
+hipError_t launch_rope_append(const RopeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 // Prefill launch shape: query heads packed per tile row block, and 32-row blocks per wave.

@@ -180,6 +180,43 @@ attn_sink_status attn_sink_decode_paged(
     void* out, float* lse, void* stream);
 
 /*
+ * The step before attention for new tokens: YaRN rotary position encoding of their Q and K
+ * and the append of their K and V into the paged cache ("GPT-OSS on Day 0", section
+ * "GPT-OSS on Hopper": the model encodes positions with YaRN, as DeepSeek-V3 does; the
+ * method is YaRN's published one). The pair (x[i], x[i + 32]) of a head vector at position p
+ * is rotated by the angle p * f_i; f_i = rope_theta^(-i / 32), and with yarn_factor s > 1,
+ * r_i = yarn_original_len * f_i / (2 pi) and g_i = clip((r_i - yarn_alpha) /
+ * (yarn_beta - yarn_alpha), 0, 1) give f_i <- g_i f_i + (1 - g_i) f_i / s; cos and sin are
+ * scaled by 0.1 ln s + 1 (by 1 when s <= 1).
+ *
+ *   q            bf16 [total_q, num_q_heads, 64], the new tokens; sequence b owns rows
+ *                [cu_seqlens_q[b], cu_seqlens_q[b+1]), its newest tokens: row t sits at
+ *                position kv_lens[b] - Lq_b + t.
+ *   k, v         bf16 [total_q, num_kv_heads, 64], the new tokens' K and V.
+ *   cu_seqlens_q int32 [batch + 1], kv_lens int32 [batch] on the device; kv_lens counts the
+ *                new tokens (clamped to min(max_kv_len, max_pages_per_seq * page_size)).
+ *   page_table, max_pages_per_seq, num_pages, page_size
+ *                as for attn_sink_decode_paged.
+ *   k_cache, v_cache
+ *                bf16 [num_pages, num_kv_heads, page_size, 64]: the rotated K and the V of
+ *                each new token are written at page page_table[b][p / page_size], slot
+ *                p % page_size; nothing else in the caches is touched.
+ *   q_out        bf16 [total_q, num_q_heads, 64], the rotated Q (may be q itself).
+ * Errors: rope_theta <= 1, yarn_factor <= 0, or (for yarn_factor > 1) yarn_original_len <= 0
+ * or yarn_alpha >= yarn_beta: ATTN_SINK_ERR_INVALID_ARG; head_dim != 64, page sizes as for
+ * decode, batch > 65535: ATTN_SINK_ERR_UNSUPPORTED. Enqueues one kernel.
+ */
+attn_sink_status attn_sink_rope_append(
+    const void* q, const void* k, const void* v,
+    const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    void* k_cache, void* v_cache,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_kv_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    float rope_theta, float yarn_factor, int32_t yarn_original_len, float yarn_alpha, float yarn_beta,
+    void* q_out, void* stream);
+
+/*
  * Verification of a draft tree in one step ("Accelerating Sonar through speculation", EAGLE
  * section: tree-shaped drafts need a custom attention mask, which a full-sequence mask made
  * costly). The mask is a bitmap per draft row: the q_len draft tokens are the last q_len of

@@ -166,6 +166,34 @@ def test_decode_tree_argument_errors(amd):
     assert _decode_tree(amd, ws_bytes=16) == WS_SMALL
     assert _decode_tree(amd, batch=0, tree=None) == OK        # nothing to do
 
+def _rope(amd, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, lens=FAKE, table=FAKE, max_pages=64, num_pages=100, kc=FAKE, vc=FAKE,
+             batch=2, total_q=32, max_q=16, max_kv=1024, hq=8, hkv=2, d=64, page=16, theta=150000.0, factor=32.0,
+             orig=4096, alpha=1.0, beta=32.0, q_out=FAKE, stream=None)
+    a.update(kw)
+    return amd.lib.attn_sink_rope_append(a["q"], a["k"], a["v"], a["cu_q"], a["lens"], a["table"], a["max_pages"],
+                                         a["num_pages"], a["kc"], a["vc"], a["batch"], a["total_q"], a["max_q"],
+                                         a["max_kv"], a["hq"], a["hkv"], a["d"], a["page"], a["theta"], a["factor"],
+                                         a["orig"], a["alpha"], a["beta"], a["q_out"], a["stream"])
+
+
+def test_rope_append_argument_errors(amd):
+    assert _rope(amd, d=128) == UNSUPPORTED
+    assert _rope(amd, page=8) == UNSUPPORTED
+    assert _rope(amd, batch=70000) == UNSUPPORTED
+    assert _rope(amd, theta=1.0) == INVALID
+    assert _rope(amd, theta=float("nan")) == INVALID
+    assert _rope(amd, factor=0.0) == INVALID
+    assert _rope(amd, orig=0) == INVALID
+    assert _rope(amd, alpha=32.0, beta=1.0) == INVALID
+    assert _rope(amd, hq=6, hkv=4) == INVALID
+    assert _rope(amd, max_pages=0) == INVALID
+    for name in ("q", "k", "v", "cu_q", "lens", "table", "kc", "vc", "q_out"):
+        assert _rope(amd, **{name: None}) == INVALID, name
+    # no YaRN scaling: original length and ramp bounds are not needed
+    assert _rope(amd, factor=1.0, orig=0, alpha=5.0, beta=1.0, batch=0) == OK
+    assert _rope(amd, total_q=0) == OK
+
 def test_decode_argument_errors(amd):
     assert _decode(amd, d=128) == UNSUPPORTED
     assert _decode(amd, q_len=9) == UNSUPPORTED

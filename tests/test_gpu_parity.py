@@ -512,6 +512,79 @@ def test_tree_verify_full_size_sampled(amd):
     assert_close(out, lse, ro, rl, "tree_verify")
 
 # -------------------------------------------------------------------------------------------
+# YaRN rotary encoding + append of new tokens into the paged cache
+# -------------------------------------------------------------------------------------------
+ROPE = dict(rope_theta=150000.0, yarn_factor=32.0, yarn_original_len=4096, yarn_alpha=1.0, yarn_beta=32.0)
+
+
+def run_rope(amd, inp, k_new, v_new, rope=ROPE, in_place=False):
+    kc, vc = tbits(inp["k_cache"]), tbits(inp["v_cache"])
+    q = tbits(inp["q"])
+    q_out = amd.attn_sink_rope_append(q, tbits(k_new), tbits(v_new), torch.from_numpy(inp["cu_seqlens_q"]).to(DEV),
+                                      torch.from_numpy(inp["kv_lens"]).to(DEV),
+                                      torch.from_numpy(inp["page_table"]).to(DEV), kc, vc, inp["max_q"],
+                                      inp["max_kv_len"], q_out=q if in_place else None, **rope)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return bits(q_out), bits(kc), bits(vc)
+
+
+def oracle_rope(inp, k_new, v_new, rope=ROPE):
+    freqs, m = oracle.yarn_frequencies(64, rope["rope_theta"], rope["yarn_factor"], rope["yarn_original_len"],
+                                       rope["yarn_alpha"], rope["yarn_beta"])
+    return oracle.rope_append(f64(inp["q"]), f64(k_new), f64(v_new), inp["cu_seqlens_q"], inp["kv_lens"],
+                              inp["page_table"], f64(inp["k_cache"]), f64(inp["v_cache"]), freqs, m)
+
+
+def assert_bf16_close(got_bits, ref, what):
+    got = f64(got_bits)
+    excess = np.abs(got - ref) - (ATOL + RTOL * np.abs(ref))
+    assert excess.max() <= 0, f"{what}: max excess {excess.max():.3e}"
+
+
+@pytest.mark.parametrize("hq,hkv,page_size,rope", [
+    (64, 8, 16, ROPE), (8, 8, 64, ROPE), (12, 3, 256, dict(ROPE, yarn_factor=1.0)),
+    (16, 2, 32, dict(ROPE, rope_theta=10000.0, yarn_factor=4.0, yarn_original_len=2048))])
+def test_rope_append(amd, hq, hkv, page_size, rope):
+    spec = scaled(CONFIGS["chunked_prefill"], batch=4, q_len=(1, 300), ctx_len=(0, 9000), hq=hq, hkv=hkv,
+                  page_size=page_size, seed=hq + page_size)
+    inp = make_paged_prefill(spec, q_lens=[1, 300, 0, 77])
+    T = int(inp["cu_seqlens_q"][-1])
+    rng = np.random.default_rng(7)
+    from workloads import bf16_round_bits
+    k_new = bf16_round_bits(rng.standard_normal((T, hkv, 64)).astype(np.float32))
+    v_new = bf16_round_bits(rng.standard_normal((T, hkv, 64)).astype(np.float32))
+    q_out, kc, vc = run_rope(amd, inp, k_new, v_new, rope)
+    rq, rk, rv = oracle_rope(inp, k_new, v_new, rope)
+    assert_bf16_close(q_out, rq, "rotated q")
+    assert_bf16_close(kc, rk, "k cache")
+    # V is copied: bit-exact; every slot no new token owns is unchanged (bit-exact too)
+    assert np.array_equal(f64(vc), rv)
+    P = page_size
+    new = np.zeros((inp["k_cache"].shape[0], P), dtype=bool)
+    for b, L in enumerate(inp["kv_lens"]):
+        n = int(inp["cu_seqlens_q"][b + 1] - inp["cu_seqlens_q"][b])
+        for p in range(int(L) - n, int(L)):
+            new[inp["page_table"][b, p // P], p % P] = True
+    same = lambda a, b: np.array_equal(np.transpose(a, (0, 2, 1, 3))[~new], np.transpose(b, (0, 2, 1, 3))[~new])
+    assert same(kc, inp["k_cache"]) and same(vc, inp["v_cache"])
+
+
+def test_rope_append_in_place_and_full_size(amd):
+    spec = CONFIGS["chunked_prefill"]
+    inp = make_paged_prefill(spec)
+    T = int(inp["cu_seqlens_q"][-1])
+    rng = np.random.default_rng(8)
+    from workloads import bf16_round_bits
+    k_new = bf16_round_bits(rng.standard_normal((T, spec.hkv, 64)).astype(np.float32))
+    v_new = bf16_round_bits(rng.standard_normal((T, spec.hkv, 64)).astype(np.float32))
+    q_out, kc, vc = run_rope(amd, inp, k_new, v_new, in_place=True)
+    rq, rk, rv = oracle_rope(inp, k_new, v_new)
+    assert_bf16_close(q_out, rq, "rotated q (in place)")
+    assert_bf16_close(kc, rk, "k cache")
+    assert np.array_equal(f64(vc), rv)
+
+# -------------------------------------------------------------------------------------------
 # graph capture: launches depend on host scalars only, so calls can be captured and replayed
 # -------------------------------------------------------------------------------------------
 def test_graph_capture_replays_match_eager(amd):
