@@ -8,7 +8,8 @@ order, 512-token chunks merged by log-sum-exp). One step = one attn_sink_decode_
 Other workloads (--workload): causal_prefill, window_prefill, verify, embed (two passes:
 sinks disabled, then N(0,1) sinks), chunked_prefill (2048-token chunks appended to paged
 caches of 0..6144 tokens), tree_verify (8-node draft trees per sequence, one-step
-verification), tiny_causal.
+verification), rope_append (YaRN rotary encoding of the chunked-prefill workload's 16384 new
+tokens and the append of their K/V into the paged cache), tiny_causal.
 
 Prints ONE JSON line. ``value`` is the algorithmic rate of the whole step (GB/s for the
 memory-bound paths, TFLOP/s for prefill); ``roofline`` describes the dominant kernel, timed
@@ -36,6 +37,7 @@ METRIC = "sink-attn decode HBM GB/s (% peak); prefill TFLOP/s (% bf16 MFMA peak)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 KERNEL_SOURCES = {
+    "rope": ["rope.hip", "common.hpp", "kernels.hpp"],
     "decode": ["decode.hip", "common.hpp", "kernels.hpp"],
     "prefill": ["prefill.hip", "common.hpp", "kernels.hpp"],
 }
@@ -48,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="paged_decode",
                     choices=["paged_decode", "verify", "tree_verify", "causal_prefill", "window_prefill", "embed",
-                             "chunked_prefill", "tiny_causal"])
+                             "chunked_prefill", "rope_append", "tiny_causal"])
     ap.add_argument("--kv-chunk", type=int, default=None,
                     help="split-KV chunk length for the paged workloads (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU oracle sample (wall seconds)")
@@ -114,6 +116,8 @@ def prefill_kernel_name(spec, max_seqlen):
 def dominant_kernel(name):
     if name in ("paged_decode", "verify", "tree_verify"):
         return "decode_split_kernel"
+    if name == "rope_append":
+        return "rope_append_kernel"
     if name == "chunked_prefill":
         spec = CONFIGS[name]
         return "prefill_pp_kernel" if (spec.window <= 0 and spec.q_len[1] >= 2048) else "prefill_kernel"
@@ -531,10 +535,88 @@ def bench_chunked(args, torch, amd, name):
     return res
 
 
+ROPE_ARGS = dict(rope_theta=150000.0, yarn_factor=32.0, yarn_original_len=4096, yarn_alpha=1.0, yarn_beta=32.0)
+
+
+def cpu_baseline_rope(inp, k_new, v_new, seconds, bytes_per_seq):
+    """The fp64 oracle, one sequence at a time (a compact pool of the sequence's pages)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    f64 = lambda b: bf16_bits_to_f32(b).astype(np.float64)
+    q, kn, vn = f64(inp["q"]), f64(k_new), f64(v_new)
+    freqs, m = oracle.yarn_frequencies(64, ROPE_ARGS["rope_theta"], ROPE_ARGS["yarn_factor"],
+                                       ROPE_ARGS["yarn_original_len"], ROPE_ARGS["yarn_alpha"], ROPE_ARGS["yarn_beta"])
+    cu, lens = inp["cu_seqlens_q"], inp["kv_lens"]
+    P = inp["k_cache"].shape[2]
+    done, n = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < seconds:
+            b = n % len(lens)
+            L = int(lens[b])
+            pages = inp["page_table"][b, :(L + P - 1) // P]
+            r0, r1 = int(cu[b]), int(cu[b + 1])
+            oracle.rope_append(q[r0:r1], kn[r0:r1], vn[r0:r1], np.array([0, r1 - r0]), lens[b:b + 1],
+                               np.arange(len(pages))[None, :], f64(inp["k_cache"][pages]), f64(inp["v_cache"][pages]),
+                               freqs, m)
+            done += bytes_per_seq[b]
+            n += 1
+    dt = time.perf_counter() - t0
+    return done / dt / 1e9, n, dt
+
+
+def bench_rope(args, torch, amd, name):
+    spec = CONFIGS["chunked_prefill"]
+    inp = make_paged_prefill(spec)
+    dev = torch.device("cuda:0")
+    T = int(inp["cu_seqlens_q"][-1])
+    rng = np.random.default_rng(11)
+    from workloads import bf16_round_bits
+    k_new = bf16_round_bits(rng.standard_normal((T, spec.hkv, 64)).astype(np.float32))
+    v_new = bf16_round_bits(rng.standard_normal((T, spec.hkv, 64)).astype(np.float32))
+    q, kn, vn = tbits(torch, inp["q"], dev), tbits(torch, k_new, dev), tbits(torch, v_new, dev)
+    kc, vc = tbits(torch, inp["k_cache"], dev), tbits(torch, inp["v_cache"], dev)
+    cu = torch.from_numpy(inp["cu_seqlens_q"]).to(dev)
+    lens = torch.from_numpy(inp["kv_lens"]).to(dev)
+    table = torch.from_numpy(inp["page_table"]).to(dev)
+    q_out = torch.empty_like(q)
+
+    def step():
+        amd.attn_sink_rope_append(q, kn, vn, cu, lens, table, kc, vc, inp["max_q"], inp["max_kv_len"], q_out=q_out,
+                                  **ROPE_ARGS)
+
+    q_lens = inp["q_lens"].astype(np.int64)
+    row_bytes = (spec.hq * 64 * 2) * 2 + (spec.hkv * 64 * 2) * 4     # q in + out, k/v in + cache out
+    bytes_seq = q_lens * row_bytes + q_lens * 4                      # + one page id per token
+    algo_bytes = int(bytes_seq.sum() + 4 * (2 * spec.batch + 1))
+    ms = time_calls(torch, step, args.steps, args.warmup)
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: YaRN rotary encoding (theta 150000, factor 32, original 4096) of {T} new "
+                               f"tokens ({spec.batch} chunks of 2048 on 0..6144 cached), {spec.hq}/{spec.hkv} heads, "
+                               f"d 64, K/V appended into 16-token pages",
+                   "algorithmic_bytes": algo_bytes},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"kernel": "rope_append_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, "rope"),
+                     "algorithmic_bytes_per_launch": algo_bytes, "kernel_ms": round(ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        v, n, dt = cpu_baseline_rope(inp, k_new, v_new, args.cpu_seconds, bytes_seq)
+        res["cpu_baseline"] = {"value": round(v, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} sequences' chunks (cycled from sequence 0), {dt:.1f} s wall, fp64 "
+                                         f"NumPy, BLAS limited to 1 thread"}
+    return res
+
+
 def main():
     args = parse()
     if args.record_traffic:
-        kind = "decode" if args.workload in ("paged_decode", "verify", "tree_verify") else "prefill"
+        kind = ("decode" if args.workload in ("paged_decode", "verify", "tree_verify") else
+                "rope" if args.workload == "rope_append" else "prefill")
         record_traffic(args.workload, kind, *args.record_traffic)
         return
     if args.gpus != 1:
@@ -557,6 +639,8 @@ def main():
         res = bench_paged(args, torch, amd, args.workload)
     elif args.workload == "chunked_prefill":
         res = bench_chunked(args, torch, amd, args.workload)
+    elif args.workload == "rope_append":
+        res = bench_rope(args, torch, amd, args.workload)
     else:
         res = bench_varlen(args, torch, amd, args.workload)
     print(json.dumps(res), flush=True)
