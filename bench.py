@@ -131,7 +131,8 @@ def record_traffic(name, kind, fetch_dir, write_dir, copy_fetch_dir, copy_write_
     kernel = dominant_kernel(name)
 
     def mean_for(directory, counter, pattern):
-        v = [val for (k, val) in _pmc_per_dispatch(directory, counter).values() if ("::" + pattern + "<") in k]
+        v = [val for (k, val) in _pmc_per_dispatch(directory, counter).values()
+             if ("::" + pattern + "<") in k or ("::" + pattern + "(") in k]
         if not v:
             raise SystemExit(f"no {counter} dispatch of {pattern} under {directory}")
         return float(np.mean(v)), len(v)
