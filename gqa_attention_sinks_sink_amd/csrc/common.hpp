@@ -146,18 +146,6 @@ __device__ __forceinline__ void buffer_load16_lds_async_nt(__amdgpu_buffer_rsrc_
       : "memory");
 }
 
-// Workgroup barrier that is also a compiler barrier for memory accesses, without the
-// s_waitcnt vmcnt(0) / lgkmcnt(0) that __syncthreads() adds.
-// 16-byte buffer load (at byte offset voff + OFF of r) that the compiler does not track: the
-// caller retires it with an explicit s_waitcnt vmcnt and calls tie() on the value before use.
-template <int OFF>
-__device__ __forceinline__ u32x4 buffer_load16_untracked(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  u32x4 v;
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3" : "=v"(v) : "v"(voff), "s"(r), "i"(OFF) : "memory");
-  return v;
-}
-// Marks v as written here, so that no use of v moves above this point.
-__device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
 
 // Lane index that the compiler can neither hoist nor keep alive across a loop: per-lane
 // addresses derived from it are recomputed where they are used.
@@ -167,10 +155,14 @@ __device__ __forceinline__ int opaque_lane_id() {
   return l;
 }
 
+// Workgroup barrier that is also a compiler barrier for memory accesses, without the
+// s_waitcnt vmcnt(0) / lgkmcnt(0) that __syncthreads() adds.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // s_waitcnt vmcnt(n) (n < 16), leaving the other counters alone.
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
+// s_waitcnt lgkmcnt(0) alone (the vmcnt field at its maximum, 63).
+#define WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14))
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 

@@ -54,9 +54,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // (16 lanes, 16 rows, one chunk) and the 8 B transposing V reads (32 lanes, 4 rows,
   // 64 B each) hit 64 distinct banks.
   __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[kStages][kStageBytes];
-  // Per-wave staging of the output rows (32 RB rows x 128 bytes per wave). With RB = 1 it
-  // fits the last ring stage, which no wave writes again before the next pass's first
-  // barrier; that keeps the LDS of three workgroups within one CU.
+  // Per-wave slice of 32 RB rows x 128 bytes: the wave's Q rows at the start of a pass, its
+  // output rows at the end. With RB = 1 the slices fill the last ring stage, which holds no
+  // tile until the first iteration issues the third one; that keeps the LDS of three
+  // workgroups within one CU.
   __shared__ __attribute__((aligned(16))) unsigned char out_lds[kThreads / 64][RB == 1 ? 16 : 32 * RB * kHeadDim * 2];
   static_assert(kStageBytes >= (kThreads / 64) * 32 * kHeadDim * 2, "RB = 1 staging fits one ring stage");
 
@@ -134,27 +135,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     vl = (p.window > 0) ? max(0, pos - p.window + 1) : 0;
     if (vh < vl) vh = vl;
   };
-  // Q^T as the B operand: column = row, k = head dim (16 per step). Rows past the end load
-  // the last valid row (their results are never stored). The loads are untracked, so that
-  // waiting for them does not also wait for the K/V tiles issued after them; qb is tied
-  // after each tile wait, which covers them.
-  u32x4 qb[RB][4];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = (w * RB + rb) * 32 + r32;
-    const int t = min(ts + r / GP, te - 1);
-    const uint32_t voff = ((uint32_t)t * p.hq + head0 + (r % GP)) * (kHeadDim * 2) + half * 16;
-    qb[rb][0] = buffer_load16_untracked<0>(rq, voff);
-    qb[rb][1] = buffer_load16_untracked<32>(rq, voff);
-    qb[rb][2] = buffer_load16_untracked<64>(rq, voff);
-    qb[rb][3] = buffer_load16_untracked<96>(rq, voff);
+  // The wave's slice: row i holds wave row i (row block i / 32); 16-byte chunk c of a row
+  // sits at chunk position c ^ (i & 7).
+  unsigned char* slice;
+  if constexpr (RB == 1) {
+    slice = kv_lds[kStages - 1] + w * (32 * kHeadDim * 2);
+  } else {
+    slice = out_lds[w];
   }
-  auto tie_q = [&]() {
+  // Q rows of the pass into the slice by DMA, issued before the first K/V tiles (so they
+  // have landed once tile 0 has) and read into registers at the first tile. Rows past the
+  // end load the last valid row (their results are never stored). Addresses come from a
+  // fresh lane id (the compiler would otherwise keep them in spill slots across the loop).
+  {
+    WAIT_LGKMCNT0();  // this wave's reads of the slice (previous pass's output) are done
+    const int ln = opaque_lane_id();
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) tie(qb[rb][ks]);
-  };
+    for (int k = 0; k < 4 * RB; ++k) {
+      const int i = 8 * k + (ln >> 3);
+      const int r = (w * RB + (i >> 5)) * 32 + (i & 31);
+      const int t = min(ts + r / GP, te - 1);
+      const uint32_t voff =
+          ((uint32_t)t * p.hq + head0 + (r % GP)) * (kHeadDim * 2) + (uint32_t)(((ln & 7) ^ (ln >> 3)) << 4);
+      buffer_load16_lds_async(rq, slice + k * 1024, voff);
+    }
+  }
+  // Q^T as the B operand: column = row, k = head dim (16 per step).
+  u32x4 qb[RB][4];
   float m[RB], lsum[RB];
   f32x16 o[RB][2];
   int hi_min = 0x7fffffff, lo_max = -0x7fffffff, hi_max = -0x7fffffff, lo_min = 0x7fffffff;
@@ -244,6 +251,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   issue_tile(jb, 0);
   if (jb + kTileN < je) issue_tile(jb + kTileN, 1);
 
+  // Q into registers once its loads (issued before the tiles) are done. The reads complete
+  // before this wave reaches the first barrier, after which (RB = 1) the third tile may
+  // overwrite the slices.
+  if (jb + kTileN < je) {
+    WAIT_VMCNT(8);
+  } else {
+    WAIT_VMCNT(4);
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qb[rb][ks] = *reinterpret_cast<const u32x4*>(slice + (rb * 32 + r32) * 128 + (((2 * ks + half) ^ (r32 & 7)) << 4));
+  WAIT_LGKMCNT0();
+
   int st = 0;
   for (int jt = jb; jt < je; jt += kTileN) {
     // This wave's loads of the current tile are done once at most the 4 loads of the next
@@ -255,7 +277,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       WAIT_VMCNT(0);
     }
     lds_barrier();
-    tie_q();
     if (jt + 2 * kTileN < je) issue_tile(jt + 2 * kTileN, st == 0 ? 2 : st - 1);
     const unsigned char* kt_lds = kv_lds[st];
     const unsigned char* vt_lds = kv_lds[st] + kTileBytes;
@@ -376,7 +397,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Retire the loads past the last tile and let every wave finish with the ring before it
   // is reused.
   WAIT_VMCNT(0);
-  tie_q();
   __syncthreads();
 
   // Epilogue: out = O / d, lse = m + log2(d) converted to natural log. O goes through this
@@ -388,12 +408,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // key loop and keep them in spill slots.)
     const int ln = opaque_lane_id();
     const int hf = ln >> 5;
-    unsigned char* ow;
-    if constexpr (RB == 1) {
-      ow = kv_lds[kStages - 1] + w * (32 * kHeadDim * 2);
-    } else {
-      ow = out_lds[w];
-    }
+    unsigned char* ow = slice;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float lt = lsum[rb] + shfl_xor(lsum[rb], 32);
