@@ -62,7 +62,11 @@ inline bool decode_layout(int32_t batch, int32_t q_len, int32_t max_kv_len, int3
   return true;
 }
 
-inline attn_sink_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP; }
+// Launchers return hipErrorInvalidConfiguration for a grid beyond the launch limits.
+inline attn_sink_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_SINK_OK;
+  return e == hipErrorInvalidConfiguration ? ATTN_SINK_ERR_UNSUPPORTED : ATTN_SINK_ERR_HIP;
+}
 
 }  // namespace
 

@@ -155,6 +155,15 @@ __device__ __forceinline__ int opaque_lane_id() {
   return l;
 }
 
+// Read of memory that no kernel writes while it runs (page tables): through the constant
+// address space, so that a wave-uniform index becomes a scalar load. A plain global load
+// here would be a vector load, and the compiler's wait for it would also retire every K/V
+// load issued before it.
+template <typename T>
+__device__ __forceinline__ T load_invariant(const T* base, size_t idx) {
+  return ((const __attribute__((address_space(4))) T*)base)[idx];
+}
+
 // Workgroup barrier that is also a compiler barrier for memory accesses, without the
 // s_waitcnt vmcnt(0) / lgkmcnt(0) that __syncthreads() adds.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }

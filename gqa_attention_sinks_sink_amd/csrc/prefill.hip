@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // buffer range stops at the sequence's last key, so rows past it read as zeros.
       const int kr = jt + 16 * w;
       const int slot = min(kr >> p.page_shift, p.max_pages - 1);
-      const int pid = clampi(p.page_table[(size_t)b * p.max_pages + slot], 0, p.num_pages - 1);
+      const int pid = clampi(load_invariant(p.page_table, (size_t)b * p.max_pages + slot), 0, p.num_pages - 1);
       const uint32_t valid = (uint32_t)clampi(Lk - kr, 0, 16);
       const size_t blk = (((size_t)pid * p.hkv + kvh) * p.page_size + (kr & (p.page_size - 1))) * kHeadDim;
       const __amdgpu_buffer_rsrc_t pk_r = make_rsrc_uniform(p.k + blk, valid * (kHeadDim * 2));
@@ -475,11 +475,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int half = lane >> 5;
   const int r32 = lane & 31;
 
+  // Work item -> (sequence, head group, unit). Workgroup L runs on XCD L % 8. The (sequence,
+  // head group) pairs are dealt to the XCDs round-robin, all units of a pair to the same XCD:
+  // the workgroups sharing one head's K/V share one L2, and every XCD gets a share of every
+  // sequence, so sequences of unequal length (chunks on different context lengths) do not
+  // load the XCDs unequally.
   const int n_hg = p.hkv * (p.group / GP);
-  const int per_xcd = gridDim.x / 8;
-  const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int unit = item % p.units;
-  const int bh = item / p.units;
+  const int j_xcd = blockIdx.x / 8;
+  const int unit = j_xcd % p.units;
+  const int bh = (int)(blockIdx.x % 8) + 8 * (j_xcd / p.units);
   if (bh >= p.batch * n_hg) return;
   const int b = bh / n_hg;
   const int hg = bh - b * n_hg;
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // power of two >= 16 keys); the buffer range ends at the sequence's last key.
         const int kr = jb + t * kTileN + 8 * w;
         const int slot = min(kr >> p.page_shift, p.max_pages - 1);
-        const int pid = clampi(p.page_table[(size_t)b * p.max_pages + slot], 0, p.num_pages - 1);
+        const int pid = clampi(load_invariant(p.page_table, (size_t)b * p.max_pages + slot), 0, p.num_pages - 1);
         const uint32_t valid = (uint32_t)clampi(Lk - kr, 0, 8);
         const size_t blk = (((size_t)pid * p.hkv + kvh) * p.page_size + (kr & (p.page_size - 1))) * kHeadDim;
         const int ln = opaque_lane_id();
@@ -881,6 +885,7 @@ hipError_t launch_rb(PrefillParams p, int gp, hipStream_t stream) {
   p.pair_blocks = (p.causal && p.window == 0) ? 1 : 0;
   p.units = p.pair_blocks ? (n_blk + 1) / 2 : n_blk;
   const long items = (long)p.units * p.batch * p.hkv * (p.group / gp);
+  if (items > 0x7ffffff0L) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)(8 * ((items + 7) / 8))), block(kThreads);
   switch (gp) {
     case 1: hipLaunchKernelGGL((prefill_kernel<1, RB, PAGED>), grid, block, 0, stream, p); break;
@@ -898,8 +903,10 @@ hipError_t launch_pp(PrefillParams p, int gp, hipStream_t stream) {
   const int n_blk = (p.max_q + tok - 1) / tok;
   p.pair_blocks = p.causal ? 1 : 0;
   p.units = p.pair_blocks ? (n_blk + 1) / 2 : n_blk;
-  const long items = (long)p.units * p.batch * p.hkv * (p.group / gp);
-  dim3 grid((unsigned)(8 * ((items + 7) / 8))), block(512);
+  const long pairs = (long)p.batch * p.hkv * (p.group / gp);  // (sequence, head group)
+  const long groups = 8 * ((pairs + 7) / 8) * (long)p.units;
+  if (groups > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)groups), block(512);
   switch (gp) {
     case 1: hipLaunchKernelGGL((prefill_pp_kernel<1, PAGED>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((prefill_pp_kernel<2, PAGED>), grid, block, 0, stream, p); break;
