@@ -35,6 +35,8 @@
 //   * The 4 wave states are combined in a fixed order ((w0 + w1) + (w2 + w3),
 //     bit-reproducible) through LDS and the chunk partial (o/d, m + ln d) goes to the
 //     workspace at the plan's offset.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -556,13 +558,15 @@ struct DeviceShape {
   int blocks_per_cu[2][5] = {{0, 0, 0, 0, 0}, {0, 0, 0, 0, 0}};  // [tree][column tiles]
 };
 
-// Per-device launch shape, computed once per device from host-side queries.
+// Per-device launch shape, computed once per device from host-side queries (call_once: the
+// library may be called from several host threads).
 const DeviceShape& device_shape() {
   static DeviceShape shapes[64];
+  static std::once_flag once[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   DeviceShape& s = shapes[dev];
-  if (s.cus == 0) {
+  std::call_once(once[dev], [&]() {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
     s.blocks_per_cu[0][1] = resident_blocks_per_cu<1, false>();
@@ -574,7 +578,7 @@ const DeviceShape& device_shape() {
     s.blocks_per_cu[1][3] = resident_blocks_per_cu<3, true>();
     s.blocks_per_cu[1][4] = resident_blocks_per_cu<4, true>();
     s.cus = cus;
-  }
+  });
   return s;
 }
 }  // namespace
