@@ -515,8 +515,12 @@ void decode_split_kernel(DecodeParams p) {
     if (w == 2) put(1);
     wait_lgkm0();
     lds_barrier();
+    if (w == 0) fold(1);
+    // Slot 1 is written again by wave 3 before the next item's first barrier (at once, when it
+    // has no group of that item): every wave waits here until wave 0 has read it.
+    wait_lgkm0();
+    lds_barrier();
     if (w == 0) {
-      fold(1);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int col = nt * 16 + col_lo;
@@ -534,8 +538,9 @@ void decode_split_kernel(DecodeParams p) {
         }
       }
     }
-    // slot 0 is read by wave 0 before the second barrier and written by wave 1 only after the
-    // next item's groups; slot 1 is written by wave 2 after the next item's first barrier.
+    // Slot 0 is read by wave 0 before the second barrier and written next by wave 1 before the
+    // next item's first barrier, which wave 1 reaches only after that second barrier; slot 1 is
+    // free once the third barrier is passed.
     cur = nxt;
     pid = pid_next;
     pid_seg = 0;
