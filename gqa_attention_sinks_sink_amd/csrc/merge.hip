@@ -5,7 +5,7 @@
 // 16 threads per (row, head), 4 head-dim elements (16 B) per thread. Partials are read
 // 8 at a time with independent loads and folded into a running (max, weight sum, sum)
 // triple, so a row of n partials costs ceil(n / 8) memory round trips. Partials at -inf
-// weigh 0; a row with no live partial yields out = 0, lse = -inf.
+// weigh 0 whatever their o holds; a row with no live partial yields out = 0, lse = -inf.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,6 +37,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
       if (i < p1) {
         l[u] = p.lse_part[(size_t)i * p.hq + h] * kLog2e;
         o[u] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)i * p.hq + h) * kHeadDim + d4);
+        if (!(l[u] > kNegInf)) {  // an empty partial (or a NaN lse): weight 0, its o unused
+          l[u] = kNegInf;
+          o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       } else {
         l[u] = kNegInf;
         o[u] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -268,8 +268,9 @@ size_t attn_sink_decode_workspace_size(int32_t batch, int32_t q_len, int32_t max
  * sinks": attention split into several blocks along the sequence). For row r and head h,
  * over partials p in [partial_indptr[r], partial_indptr[r+1]):
  *     LSE = ln sum_p exp(lse_partial[p][h]),  out = sum_p exp(lse_partial[p][h] - LSE) o_partial[p][h]
- * Partials with lse = -inf carry weight 0; a row whose partials are all -inf (or that has
- * none) returns out = 0, lse = -inf.
+ * Partials with lse = -inf (or NaN) carry weight 0 and their o is not used (it may hold
+ * anything, NaN included); a row whose partials are all -inf (or that has none) returns
+ * out = 0, lse = -inf.
  *
  *   o_partial    fp32 [num_partials, num_q_heads, 64]; each partial already normalised.
  *   lse_partial  fp32 [num_partials, num_q_heads], natural log.

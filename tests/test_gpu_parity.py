@@ -397,6 +397,21 @@ def test_merge_all_empty_rows(amd):
     assert torch.all(out.float() == 0) and torch.all(torch.isneginf(lse))
 
 
+def test_merge_ignores_the_output_of_empty_partials(amd):
+    # row 0: a live partial and an empty one whose o is NaN; row 1: only the NaN-o empty one
+    o = torch.empty(3, 2, 64, device=DEV)
+    o[0] = torch.linspace(-1, 1, 64, device=DEV)
+    o[1:] = float("nan")
+    l = torch.tensor([[0.5, -1.0], [float("-inf"), float("-inf")], [float("-inf"), float("nan")]], device=DEV)
+    indptr = torch.tensor([0, 2, 3], dtype=torch.int32, device=DEV)
+    out, lse = amd.attn_sink_merge_partials(o, l, indptr)
+    torch.cuda.synchronize()
+    ref = o[0].to(torch.bfloat16)
+    assert torch.equal(out[0], ref)
+    assert torch.allclose(lse[0], l[0], atol=1e-6, rtol=0)
+    assert torch.all(out[1].float() == 0) and torch.all(torch.isneginf(lse[1]))
+
+
 def test_page_permutation_bit_identical(amd):
     spec = scaled(CONFIGS["verify"], kv_chunk=512, batch=4, kv_len=(50, 1200), hq=16, hkv=2, seed=65)
     inp = make_paged(spec)
