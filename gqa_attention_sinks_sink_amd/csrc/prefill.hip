@@ -283,7 +283,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     st = (st == kStages - 1) ? 0 : st + 1;
 
     if (jt < hi_max && jt + kTileN > lo_min) {
-      const bool need_mask = !(jt >= lo_max && jt + kTileN <= hi_min);
+      // a 32-key half needs the mask unless every row of the wave sees all of it
+      const bool need_mask0 = !(jt >= lo_max && jt + 32 <= hi_min);
+      const bool need_mask1 = !(jt + 32 >= lo_max && jt + kTileN <= hi_min);
       f32x16 s[RB][2];  // S^T per row block and 32-key half
       // S^T for one 32-key half: k = 64 in 4 steps; each K fragment serves every row block.
       auto qk_half = [&](int kt) {
@@ -382,10 +384,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // Software pipeline inside the tile: the exps of one half run in the shadow of the
       // MFMAs of other work (S of the second half, then PV of the first half).
       qk_half(0);
-      if (need_mask) mask_half(0);
+      if (need_mask0) mask_half(0);
       qk_half(1);
       softmax_half(0);
-      if (need_mask) mask_half(1);
+      if (need_mask1) mask_half(1);
       pv_step(0);
       pv_step(1);
       softmax_half(1);
