@@ -86,7 +86,8 @@ typedef enum {
  * softmax_scale finite and > 0; q, k, v, out and the cu_seqlens pointers non-NULL when
  * batch > 0 and total_q > 0. One sequence's Q rows (max_seqlen_q * num_q_heads * 128
  * bytes) and K or V rows (plus one 64-key tile) must each span less than 2^31 bytes,
- * else ATTN_SINK_ERR_UNSUPPORTED.
+ * and the launch (one workgroup per block of up to 512 query rows of one KV head, per
+ * sequence) must stay under 2^31 workgroups, else ATTN_SINK_ERR_UNSUPPORTED.
  */
 attn_sink_status attn_sink_prefill(
     const void* q, const void* k, const void* v, const float* sinks,
@@ -117,7 +118,8 @@ attn_sink_status attn_sink_prefill(
  *   sinks, softmax_scale, causal, window, out, lse
  *                as for attn_sink_prefill.
  * No workspace: every chunk's rows are finished in one pass. Errors as above; one
- * sequence's Q rows must span less than 2^31 bytes.
+ * sequence's Q rows must span less than 2^31 bytes and the launch stay under 2^31
+ * workgroups (as for attn_sink_prefill).
  */
 attn_sink_status attn_sink_prefill_paged(
     const void* q, const void* k_cache, const void* v_cache,
