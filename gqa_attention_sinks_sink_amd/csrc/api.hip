@@ -21,6 +21,8 @@ constexpr int32_t kMaxColumns = 64;   // q_len * (num_q_heads / num_kv_heads) pe
 constexpr int64_t kMaxGridY = 65535;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// The kernels move bf16 rows and fp32 partials in 16-byte pieces.
+inline bool misaligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
 
 inline bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -97,6 +99,7 @@ attn_sink_status attn_sink_prefill(const void* q, const void* k, const void* v, 
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
   if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr) return ATTN_SINK_ERR_INVALID_ARG;
   if (total_kv > 0 && (k == nullptr || v == nullptr)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out)) return ATTN_SINK_ERR_INVALID_ARG;
   // Q, K and V of one sequence are addressed with 32-bit byte offsets.
   if ((int64_t)max_seqlen_kv * num_kv_heads * kSupportedHeadDim * 2 + 64ll * num_kv_heads * kSupportedHeadDim * 2 > INT32_MAX)
     return ATTN_SINK_ERR_UNSUPPORTED;
@@ -146,6 +149,8 @@ attn_sink_status attn_sink_prefill_paged(const void* q, const void* k_cache, con
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || page_table == nullptr || kv_lens == nullptr ||
       cu_seqlens_q == nullptr || out == nullptr)
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache) || misaligned16(out))
     return ATTN_SINK_ERR_INVALID_ARG;
   // One sequence's Q rows are addressed with 32-bit byte offsets.
   if ((int64_t)max_seqlen_q * num_q_heads * kSupportedHeadDim * 2 > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
@@ -203,6 +208,9 @@ attn_sink_status attn_sink_rope_append(const void* q, const void* k, const void*
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
   if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr || kv_lens == nullptr ||
       page_table == nullptr || k_cache == nullptr || v_cache == nullptr || q_out == nullptr)
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(k_cache) || misaligned16(v_cache) ||
+      misaligned16(q_out))
     return ATTN_SINK_ERR_INVALID_ARG;
 
   RopeParams p{};
@@ -282,6 +290,8 @@ attn_sink_status decode_prepare(const void* q, const void* k_cache, const void* 
   if (batch == 0) return ATTN_SINK_OK;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || page_table == nullptr || kv_lens == nullptr ||
       (out_required && out == nullptr) || workspace == nullptr)
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache) || (out != nullptr && misaligned16(out)))
     return ATTN_SINK_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_SINK_ERR_INVALID_ARG;
   if (workspace_bytes < attn_sink_decode_workspace_size(batch, q_len, max_kv_len, num_q_heads, head_dim, kv_chunk) ||
@@ -409,6 +419,7 @@ attn_sink_status attn_sink_merge_partials(const float* o_partial, const float* l
   if (num_rows == 0) return ATTN_SINK_OK;
   if (partial_indptr == nullptr || out == nullptr) return ATTN_SINK_ERR_INVALID_ARG;
   if (num_partials > 0 && (o_partial == nullptr || lse_partial == nullptr)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned16(o_partial) || misaligned16(out)) return ATTN_SINK_ERR_INVALID_ARG;
   MergeParams mp;
   mp.o_part = o_partial;
   mp.lse_part = lse_partial;

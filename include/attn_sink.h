@@ -32,6 +32,8 @@
  *   - A query row with no visible key returns out = 0 and lse = sink[h] (-inf when the
  *     sink is disabled); no NaN is produced.
  *   - head_dim must be 64.
+ *   - bf16 tensors (q, k, v, the caches, out, q_out) and o_partial must start on a 16-byte
+ *     boundary (every torch allocation does), else ATTN_SINK_ERR_INVALID_ARG.
  *   - Errors: arguments are validated on the host before anything is enqueued; invalid
  *     arguments return ATTN_SINK_ERR_INVALID_ARG and unsupported shapes
  *     ATTN_SINK_ERR_UNSUPPORTED, with nothing launched. A failed launch returns

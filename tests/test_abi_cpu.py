@@ -255,6 +255,26 @@ def test_merge_argument_errors(amd):
     assert f(None, None, 0, None, 0, 8, 64, None, None, None) == OK
 
 
+def test_misaligned_tensors_are_rejected(amd):
+    # bf16 rows and fp32 partials move in 16-byte pieces: pointers off a 16-byte boundary are refused
+    odd = FAKE + 2
+    assert _prefill(amd, q=odd) == INVALID
+    assert _prefill(amd, k=odd) == INVALID
+    assert _prefill(amd, out=odd) == INVALID
+    assert _prefill_paged(amd, kc=odd) == INVALID
+    assert _prefill_paged(amd, out=odd) == INVALID
+    assert _decode(amd, q=odd) == INVALID
+    assert _decode(amd, v=odd) == INVALID
+    assert _decode(amd, out=odd) == INVALID
+    assert _decode_tree(amd, k=odd) == INVALID
+    assert _rope(amd, q=odd) == INVALID
+    assert _rope(amd, vc=odd) == INVALID
+    assert _rope(amd, q_out=odd) == INVALID
+    f = amd.lib.attn_sink_merge_partials
+    assert f(odd, FAKE, 10, FAKE, 4, 8, 64, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 10, FAKE, 4, 8, 64, odd, None, None) == INVALID
+
+
 def test_binding_refuses_cpu_tensors(amd):
     import torch
     q = torch.zeros(16, 4, 64, dtype=torch.bfloat16)
