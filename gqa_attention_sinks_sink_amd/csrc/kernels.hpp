@@ -49,6 +49,7 @@ struct PrefillParams {
   float scale_log2;
   int units;        // work units per (sequence, head group); set by the launcher
   int pair_blocks;  // causal pairing of row blocks u and n-1-u; set by the launcher
+  int xcd_round_robin;  // 8-wave kernel: deal (sequence, head group) pairs to XCDs round-robin
   // Paged K/V (chunked prefill) when page_table != nullptr: k and v are caches
   // [num_pages, hkv, page_size, 64], sequence b holds kv_lens[b] tokens (its queries are the
   // newest ones) and cu_kv / total_kv are unused.

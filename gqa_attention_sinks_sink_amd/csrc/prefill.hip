@@ -477,15 +477,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int half = lane >> 5;
   const int r32 = lane & 31;
 
-  // Work item -> (sequence, head group, unit). Workgroup L runs on XCD L % 8. The (sequence,
-  // head group) pairs are dealt to the XCDs round-robin, all units of a pair to the same XCD:
-  // the workgroups sharing one head's K/V share one L2, and every XCD gets a share of every
-  // sequence, so sequences of unequal length (chunks on different context lengths) do not
-  // load the XCDs unequally.
+  // Work item -> (sequence, head group, unit). Workgroup L runs on XCD L % 8. When the
+  // (sequence, head group) pairs come in multiples of 8, they are dealt to the XCDs round-robin,
+  // all units of a pair to the same XCD: the workgroups sharing one head's K/V share one L2, and
+  // every XCD gets an equal share of pairs from every sequence, so sequences of unequal length
+  // (chunks on different context lengths) do not load the XCDs unequally. Otherwise (few pairs)
+  // the items, numbered pair-major, are dealt in contiguous ranges, which splits a pair's units
+  // over several XCDs rather than leaving XCDs idle.
   const int n_hg = p.hkv * (p.group / GP);
-  const int j_xcd = blockIdx.x / 8;
-  const int unit = j_xcd % p.units;
-  const int bh = (int)(blockIdx.x % 8) + 8 * (j_xcd / p.units);
+  int unit, bh;
+  if (p.xcd_round_robin) {
+    const int j_xcd = blockIdx.x / 8;
+    unit = j_xcd % p.units;
+    bh = (int)(blockIdx.x % 8) + 8 * (j_xcd / p.units);
+  } else {
+    const int item = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+    unit = item % p.units;
+    bh = item / p.units;
+  }
   if (bh >= p.batch * n_hg) return;
   const int b = bh / n_hg;
   const int hg = bh - b * n_hg;
@@ -906,9 +915,10 @@ hipError_t launch_pp(PrefillParams p, int gp, hipStream_t stream) {
   p.pair_blocks = p.causal ? 1 : 0;
   p.units = p.pair_blocks ? (n_blk + 1) / 2 : n_blk;
   const long pairs = (long)p.batch * p.hkv * (p.group / gp);  // (sequence, head group)
-  const long groups = 8 * ((pairs + 7) / 8) * (long)p.units;
-  if (groups > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  dim3 grid((unsigned)groups), block(512);
+  p.xcd_round_robin = (pairs % 8 == 0) ? 1 : 0;
+  const long items = pairs * (long)p.units;  // a multiple of 8 when dealing pairs round-robin
+  if (items > 0x7ffffff0L) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)(8 * ((items + 7) / 8))), block(512);
   switch (gp) {
     case 1: hipLaunchKernelGGL((prefill_pp_kernel<1, PAGED>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((prefill_pp_kernel<2, PAGED>), grid, block, 0, stream, p); break;
