@@ -15,20 +15,21 @@ from typing import Optional, Tuple
 
 import torch
 
-from .build import LIB_LOAD_PATH as LIB_PATH
+from .build import LIB_PATH
 
 __all__ = [
     "lib", "AttnSinkError", "attn_sink_prefill", "attn_sink_prefill_paged", "attn_sink_decode_paged",
     "attn_sink_decode_paged_partials", "attn_sink_decode_paged_tree", "attn_sink_rope_append",
     "attn_sink_decode_workspace_size",
     "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version", "decode_workspace_layout",
-    "EXPORTED_SYMBOLS",
+    "attn_sink_decode_workspace_layout", "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
     "attn_sink_prefill", "attn_sink_prefill_paged", "attn_sink_decode_paged", "attn_sink_decode_paged_partials",
     "attn_sink_decode_paged_tree", "attn_sink_rope_append",
-    "attn_sink_decode_workspace_size", "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version",
+    "attn_sink_decode_workspace_size", "attn_sink_decode_workspace_layout", "attn_sink_merge_partials",
+    "attn_sink_status_string", "attn_sink_version",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -51,7 +52,7 @@ lib.attn_sink_decode_paged_tree.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp,
                                             _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _fp, _vp]
 lib.attn_sink_rope_append.restype = ctypes.c_int
 lib.attn_sink_rope_append.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                      _i32, _i32, _i32, _f32, _f32, _i32, _f32, _f32, _vp, _vp]
+                                      _i32, _i32, _i32, _f32, _f32, _i32, _f32, _f32, _i32, _vp, _vp]
 lib.attn_sink_decode_paged.restype = ctypes.c_int
 lib.attn_sink_decode_paged.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz, _vp, _fp, _vp]
@@ -60,6 +61,8 @@ lib.attn_sink_decode_paged_partials.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, 
                                                 _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz, _vp]
 lib.attn_sink_decode_workspace_size.restype = _sz
 lib.attn_sink_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+lib.attn_sink_decode_workspace_layout.restype = ctypes.c_int
+lib.attn_sink_decode_workspace_layout.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _vp]
 lib.attn_sink_merge_partials.restype = ctypes.c_int
 lib.attn_sink_merge_partials.argtypes = [_fp, _fp, _i32, _fp, _i32, _i32, _i32, _vp, _fp, _vp]
 lib.attn_sink_status_string.restype = ctypes.c_char_p
@@ -202,13 +205,18 @@ def attn_sink_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     return out, lse
 
 
+_YARN_RAMPS = {"turns": 0, "index": 1}
+
+
 def attn_sink_rope_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                           kv_lens: torch.Tensor, page_table: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                           max_seqlen_q: int, max_kv_len: int, rope_theta: float, yarn_factor: float = 1.0,
                           yarn_original_len: int = 0, yarn_alpha: float = 1.0, yarn_beta: float = 32.0,
-                          q_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                          yarn_ramp: str = "turns", q_out: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
     """q [T, hq, 64], k/v [T, hkv, 64] bf16 (new tokens); caches [pages, hkv, page_size, 64] bf16, updated in
-    place; cu_seqlens_q int32 [batch+1]; kv_lens int32 [batch] (new tokens included). Returns the rotated q."""
+    place; cu_seqlens_q int32 [batch+1]; kv_lens int32 [batch] (new tokens included); yarn_ramp "turns" or
+    "index" (ATTN_SINK_YARN_RAMP_TURNS / _INDEX). Returns the rotated q."""
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _check(t, n, torch.bfloat16, dev)
@@ -234,7 +242,7 @@ def attn_sink_rope_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_
                                    page_table.shape[1], num_pages, _ptr(k_cache), _ptr(v_cache), batch, total_q,
                                    int(max_seqlen_q), int(max_kv_len), hq, hkv, d, page_size, float(rope_theta),
                                    float(yarn_factor), int(yarn_original_len), float(yarn_alpha), float(yarn_beta),
-                                   _ptr(q_out), _stream(stream))
+                                   _YARN_RAMPS[yarn_ramp], _ptr(q_out), _stream(stream))
     _raise(st, "attn_sink_rope_append")
     return q_out
 
@@ -244,24 +252,24 @@ def attn_sink_decode_workspace_size(batch: int, q_len: int, max_kv_len: int, num
     return int(lib.attn_sink_decode_workspace_size(batch, q_len, max_kv_len, num_q_heads, head_dim, kv_chunk))
 
 
-def decode_workspace_layout(batch: int, q_len: int, max_kv_len: int, num_q_heads: int, kv_chunk: int,
-                            page_size: int = 16) -> dict:
-    """Byte offsets of the plan and partial regions inside the decode workspace (as documented in
-    attn_sink.h), for reading the plan and the partials back."""
-    a = lambda x: (x + 255) // 256 * 256
-    if kv_chunk > 0:
-        chunk = kv_chunk
-    else:
-        g = max(64, page_size)
-        chunk = -(-max(max_kv_len, 1) // g) * g
-    rows = batch * q_len
-    chunks = max(1, -(-max_kv_len // chunk))
-    partials = rows * chunks
-    off_counts = a(4 * (rows + 1))
-    off_o = off_counts + a(4 * rows)
-    off_lse = off_o + a(4 * partials * num_q_heads * 64)
-    return dict(rows=rows, chunks=chunks, partials=partials, off_indptr=0, off_counts=off_counts, off_o=off_o,
-                off_lse=off_lse, total=off_lse + a(4 * partials * num_q_heads))
+class _DecodeLayout(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in
+                ("rows", "chunks", "partials", "off_indptr", "off_counts", "off_o", "off_lse", "total")]
+
+
+def attn_sink_decode_workspace_layout(batch: int, q_len: int, max_kv_len: int, num_q_heads: int, head_dim: int,
+                                      kv_chunk: int) -> dict:
+    """Byte offsets of the plan and partial regions inside the decode workspace, from the library."""
+    lay = _DecodeLayout()
+    st = lib.attn_sink_decode_workspace_layout(batch, q_len, max_kv_len, num_q_heads, head_dim, kv_chunk,
+                                               ctypes.byref(lay))
+    _raise(st, "attn_sink_decode_workspace_layout")
+    return {name: int(getattr(lay, name)) for name, _ in _DecodeLayout._fields_}
+
+
+def decode_workspace_layout(batch: int, q_len: int, max_kv_len: int, num_q_heads: int, kv_chunk: int) -> dict:
+    """attn_sink_decode_workspace_layout for head_dim 64."""
+    return attn_sink_decode_workspace_layout(batch, q_len, max_kv_len, num_q_heads, 64, kv_chunk)
 
 
 def _decode_args(q, k_cache, v_cache, page_table, kv_lens, sinks, q_len, workspace, kv_chunk, max_kv_len):
@@ -384,7 +392,7 @@ def attn_sink_decode_paged_partials(q: torch.Tensor, k_cache: torch.Tensor, v_ca
                                              int(bool(causal)), int(window), int(kv_chunk), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream))
     _raise(st, "attn_sink_decode_paged_partials")
-    lay = decode_workspace_layout(batch, q_len, int(max_kv_len), hq, kv_chunk, page_size)
+    lay = attn_sink_decode_workspace_layout(batch, q_len, int(max_kv_len), hq, d, kv_chunk)
     ws = workspace.view(torch.uint8).reshape(-1)
     n_p = lay["partials"]
     return dict(

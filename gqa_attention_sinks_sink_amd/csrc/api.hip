@@ -193,7 +193,7 @@ attn_sink_status attn_sink_rope_append(const void* q, const void* k, const void*
                                        int32_t max_seqlen_q, int32_t max_kv_len, int32_t num_q_heads,
                                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size, float rope_theta,
                                        float yarn_factor, int32_t yarn_original_len, float yarn_alpha,
-                                       float yarn_beta, void* q_out, void* stream) {
+                                       float yarn_beta, int32_t yarn_ramp, void* q_out, void* stream) {
   if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_kv_len < 0 || max_pages_per_seq < 1 || num_pages < 1)
     return ATTN_SINK_ERR_INVALID_ARG;
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return ATTN_SINK_ERR_INVALID_ARG;
@@ -202,6 +202,8 @@ attn_sink_status attn_sink_rope_append(const void* q, const void* k, const void*
   if (yarn_factor > 1.f && !(yarn_original_len > 0 && std::isfinite(yarn_alpha) && std::isfinite(yarn_beta) &&
                              yarn_alpha < yarn_beta))
     return ATTN_SINK_ERR_INVALID_ARG;
+  if (yarn_ramp != ATTN_SINK_YARN_RAMP_TURNS && yarn_ramp != ATTN_SINK_YARN_RAMP_INDEX) return ATTN_SINK_ERR_INVALID_ARG;
+  if (yarn_factor > 1.f && yarn_ramp == ATTN_SINK_YARN_RAMP_INDEX && !(yarn_alpha > 0.f)) return ATTN_SINK_ERR_INVALID_ARG;
   if (head_dim != kSupportedHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
   if (!is_pow2(page_size) || page_size < 16 || page_size > 256) return ATTN_SINK_ERR_UNSUPPORTED;
   if (batch > kMaxGridY) return ATTN_SINK_ERR_UNSUPPORTED;
@@ -235,14 +237,18 @@ attn_sink_status attn_sink_rope_append(const void* q, const void* k, const void*
   p.page_shift = ilog2(page_size);
   // YaRN: base frequencies theta^(-2i/d); with factor s > 1, a ramp over the turns r_i each
   // pair makes in the original context keeps fast pairs (r >= beta), divides slow ones
-  // (r <= alpha) by s and blends in between; the temperature 0.1 ln s + 1 scales cos and sin.
+  // (r <= alpha) by s and blends in between, linearly in r or in ln r (the pair index); the
+  // temperature 0.1 ln s + 1 scales cos and sin.
   const double pi2 = 6.283185307179586;
   for (int i = 0; i < kSupportedHeadDim / 2; ++i) {
     const double f = std::pow((double)rope_theta, -2.0 * i / kSupportedHeadDim);
     double fi = f;
     if (yarn_factor > 1.f) {
       const double r = (double)yarn_original_len * f / pi2;
-      const double g = std::min(1.0, std::max(0.0, (r - yarn_alpha) / ((double)yarn_beta - yarn_alpha)));
+      const double t = (yarn_ramp == ATTN_SINK_YARN_RAMP_TURNS)
+                           ? (r - yarn_alpha) / ((double)yarn_beta - yarn_alpha)
+                           : std::log(r / yarn_alpha) / std::log((double)yarn_beta / yarn_alpha);
+      const double g = std::min(1.0, std::max(0.0, t));
       fi = g * f + (1.0 - g) * f / yarn_factor;
     }
     p.freqs[i] = fi;
@@ -258,6 +264,24 @@ size_t attn_sink_decode_workspace_size(int32_t batch, int32_t q_len, int32_t max
   // The page size only rounds the single-chunk length up; it never changes the chunk count.
   if (!decode_layout(batch, q_len, max_kv_len, num_q_heads, effective_chunk(kv_chunk, max_kv_len, 16), &l)) return 0;
   return l.total;
+}
+
+attn_sink_status attn_sink_decode_workspace_layout(int32_t batch, int32_t q_len, int32_t max_kv_len,
+                                                   int32_t num_q_heads, int32_t head_dim, int32_t kv_chunk,
+                                                   attn_sink_decode_layout* layout) {
+  if (layout == nullptr || head_dim != kSupportedHeadDim) return ATTN_SINK_ERR_INVALID_ARG;
+  DecodeLayout l;
+  if (!decode_layout(batch, q_len, max_kv_len, num_q_heads, effective_chunk(kv_chunk, max_kv_len, 16), &l))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  layout->rows = l.rows;
+  layout->chunks = l.chunks;
+  layout->partials = l.partials;
+  layout->off_indptr = (int64_t)l.off_indptr;
+  layout->off_counts = (int64_t)l.off_counts;
+  layout->off_o = (int64_t)l.off_o;
+  layout->off_lse = (int64_t)l.off_lse;
+  layout->total = (int64_t)l.total;
+  return ATTN_SINK_OK;
 }
 
 }  // extern "C"

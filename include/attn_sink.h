@@ -183,15 +183,27 @@ attn_sink_status attn_sink_decode_paged(
     void* workspace, size_t workspace_bytes,
     void* out, float* lse, void* stream);
 
+/* Ramp forms of YaRN's frequency blend (argument yarn_ramp of attn_sink_rope_append). */
+typedef enum {
+  ATTN_SINK_YARN_RAMP_TURNS = 0, /* g_i linear in the turns r_i (the YaRN paper's ramp function) */
+  ATTN_SINK_YARN_RAMP_INDEX = 1  /* g_i linear in the pair index i, i.e. in ln r_i */
+} attn_sink_yarn_ramp;
+
 /*
  * The step before attention for new tokens: YaRN rotary position encoding of their Q and K
  * and the append of their K and V into the paged cache ("GPT-OSS on Day 0", section
  * "GPT-OSS on Hopper": the model encodes positions with YaRN, as DeepSeek-V3 does; the
  * method is YaRN's published one). The pair (x[i], x[i + 32]) of a head vector at position p
  * is rotated by the angle p * f_i; f_i = rope_theta^(-i / 32), and with yarn_factor s > 1,
- * r_i = yarn_original_len * f_i / (2 pi) and g_i = clip((r_i - yarn_alpha) /
- * (yarn_beta - yarn_alpha), 0, 1) give f_i <- g_i f_i + (1 - g_i) f_i / s; cos and sin are
- * scaled by 0.1 ln s + 1 (by 1 when s <= 1).
+ * r_i = yarn_original_len * f_i / (2 pi) (turns of pair i over the original context) and a
+ * ramp g_i that is 1 where r_i >= yarn_beta and 0 where r_i <= yarn_alpha give
+ * f_i <- g_i f_i + (1 - g_i) f_i / s; cos and sin are scaled by 0.1 ln s + 1 (by 1 when
+ * s <= 1). Inside the band the ramp is
+ *   ATTN_SINK_YARN_RAMP_TURNS: g_i = (r_i - yarn_alpha) / (yarn_beta - yarn_alpha), or
+ *   ATTN_SINK_YARN_RAMP_INDEX: g_i = ln(r_i / yarn_alpha) / ln(yarn_beta / yarn_alpha), which is
+ *     linear in the pair index between the (real) indices where r_i = yarn_beta and
+ *     r_i = yarn_alpha (the form of released YaRN implementations that compute correction
+ *     dimensions); the page does not say which form its model uses.
  *
  *   q            bf16 [total_q, num_q_heads, 64], the new tokens; sequence b owns rows
  *                [cu_seqlens_q[b], cu_seqlens_q[b+1]), its newest tokens: row t sits at
@@ -205,10 +217,12 @@ attn_sink_status attn_sink_decode_paged(
  *                bf16 [num_pages, num_kv_heads, page_size, 64]: the rotated K and the V of
  *                each new token are written at page page_table[b][p / page_size], slot
  *                p % page_size; nothing else in the caches is touched.
+ *   yarn_ramp    an attn_sink_yarn_ramp value (ignored when yarn_factor <= 1).
  *   q_out        bf16 [total_q, num_q_heads, 64], the rotated Q (may be q itself).
- * Errors: rope_theta <= 1, yarn_factor <= 0, or (for yarn_factor > 1) yarn_original_len <= 0
- * or yarn_alpha >= yarn_beta: ATTN_SINK_ERR_INVALID_ARG; head_dim != 64, page sizes as for
- * decode, batch > 65535: ATTN_SINK_ERR_UNSUPPORTED. Enqueues one kernel.
+ * Errors: rope_theta <= 1, yarn_factor <= 0, or (for yarn_factor > 1) yarn_original_len <= 0,
+ * yarn_alpha >= yarn_beta, yarn_alpha <= 0 with the index ramp, or an unknown yarn_ramp:
+ * ATTN_SINK_ERR_INVALID_ARG; head_dim != 64, page sizes as for decode, batch > 65535:
+ * ATTN_SINK_ERR_UNSUPPORTED. Enqueues one kernel.
  */
 attn_sink_status attn_sink_rope_append(
     const void* q, const void* k, const void* v,
@@ -218,7 +232,7 @@ attn_sink_status attn_sink_rope_append(
     int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_kv_len,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
     float rope_theta, float yarn_factor, int32_t yarn_original_len, float yarn_alpha, float yarn_beta,
-    void* q_out, void* stream);
+    int32_t yarn_ramp, void* q_out, void* stream);
 
 /*
  * Verification of a draft tree in one step ("Accelerating Sonar through speculation", EAGLE
@@ -266,6 +280,28 @@ attn_sink_status attn_sink_decode_paged_partials(
  */
 size_t attn_sink_decode_workspace_size(int32_t batch, int32_t q_len, int32_t max_kv_len,
                                        int32_t num_q_heads, int32_t head_dim, int32_t kv_chunk);
+
+/* Where the decode entry points put the plan and the partials inside the workspace. */
+typedef struct {
+  int64_t rows;        /* batch * q_len query rows */
+  int64_t chunks;      /* chunk bound per row: max(1, ceil(max_kv_len / chunk length)) */
+  int64_t partials;    /* rows * chunks partial slots */
+  int64_t off_indptr;  /* byte offset of int32 partial_indptr[rows + 1] */
+  int64_t off_counts;  /* byte offset of int32 chunk_counts[rows] */
+  int64_t off_o;       /* byte offset of fp32 o_partial[partials][num_q_heads][64] */
+  int64_t off_lse;     /* byte offset of fp32 lse_partial[partials][num_q_heads] */
+  int64_t total;       /* workspace bytes (attn_sink_decode_workspace_size) */
+} attn_sink_decode_layout;
+
+/*
+ * Fills *layout for these host scalars (the layout documented at attn_sink_decode_paged, the
+ * same one the decode entry points use), so that callers read the plan and the partials back
+ * without re-deriving the offsets. Returns ATTN_SINK_ERR_INVALID_ARG for a NULL layout or
+ * scalars for which attn_sink_decode_workspace_size returns 0. Host-only; enqueues nothing.
+ */
+attn_sink_status attn_sink_decode_workspace_layout(int32_t batch, int32_t q_len, int32_t max_kv_len,
+                                                   int32_t num_q_heads, int32_t head_dim, int32_t kv_chunk,
+                                                   attn_sink_decode_layout* layout);
 
 /*
  * Log-sum-exp merge of split-KV partials ("GPT-OSS on Day 0", section "Attention

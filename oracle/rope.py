@@ -6,13 +6,20 @@ here is the published YaRN method written out directly:
   * rotary embedding: the pair (x[i], x[i + d/2]) of a head vector at position p is rotated
     by the angle p * f_i, with base frequencies f_i = theta^(-2i/d), i < d/2;
   * YaRN's frequency scaling with factor s > 1 over an original context of L0 positions:
-    with r_i = L0 * f_i / (2 pi) (how many turns dimension i makes over L0), a ramp
-    g_i = clip((r_i - alpha) / (beta - alpha), 0, 1) keeps fast dimensions (g = 1) and
-    divides slow ones by s (g = 0): f'_i = g_i f_i + (1 - g_i) f_i / s;
+    with r_i = L0 * f_i / (2 pi) (how many turns dimension i makes over L0), a ramp g_i
+    keeps fast dimensions (g = 1 where r_i >= beta) and divides slow ones by s (g = 0 where
+    r_i <= alpha): f'_i = g_i f_i + (1 - g_i) f_i / s. Two ramp forms share those limits:
+      "turns": g_i = clip((r_i - alpha) / (beta - alpha), 0, 1), linear in r_i (the ramp
+               function of the YaRN paper);
+      "index": g_i linear in the pair index i between the (real) indices where r_i = beta
+               and r_i = alpha; since ln r_i is linear in i this is
+               g_i = clip(ln(r_i / alpha) / ln(beta / alpha), 0, 1) (the form of released
+               YaRN implementations that compute correction dimensions);
   * YaRN's attention temperature: cos and sin are scaled by m = 0.1 ln(s) + 1 for both
     q and k (the logits by m^2); m = 1 when s <= 1.
-The pairing (i with i + d/2), the angle sign and every parameter value are readings stated
-in the design notes.
+The pairing (i with i + d/2), the angle sign, the ramp form and every parameter value are
+readings stated in the design notes. The ramp's interior is pinned by hand-derived fixtures
+(tests/golden/yarn_ramp.json) for both forms.
 """
 from __future__ import annotations
 
@@ -22,14 +29,20 @@ import numpy as np
 
 
 def yarn_frequencies(head_dim: int, theta: float, factor: float, orig_len: int, alpha: float,
-                     beta: float) -> Tuple[np.ndarray, float]:
-    """Per-pair angular frequencies [head_dim // 2] and the temperature m (fp64)."""
+                     beta: float, ramp: str = "turns") -> Tuple[np.ndarray, float]:
+    """Per-pair angular frequencies [head_dim // 2] and the temperature m (fp64). ``ramp`` is
+    "turns" (linear in r_i) or "index" (linear in the pair index, i.e. in ln r_i)."""
     i = np.arange(head_dim // 2, dtype=np.float64)
     f = float(theta) ** (-2.0 * i / head_dim)
     if factor <= 1.0:
         return f, 1.0
     r = orig_len * f / (2.0 * np.pi)
-    g = np.clip((r - alpha) / (beta - alpha), 0.0, 1.0)
+    if ramp == "turns":
+        g = np.clip((r - alpha) / (beta - alpha), 0.0, 1.0)
+    elif ramp == "index":
+        g = np.clip(np.log(r / alpha) / np.log(beta / alpha), 0.0, 1.0)
+    else:
+        raise ValueError(f"unknown YaRN ramp form {ramp!r}")
     return g * f + (1.0 - g) * f / factor, 0.1 * np.log(factor) + 1.0
 
 

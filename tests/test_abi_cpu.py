@@ -70,6 +70,38 @@ def test_workspace_size_layout_and_monotone(amd):
     assert ws(8, 2, 9000, 32, 64, 512) >= ws(8, 2, 9000, 16, 64, 512)
 
 
+def _documented_layout(batch, q_len, max_kv_len, hq, kv_chunk):
+    """The workspace layout as the header documents it: R = batch * q_len rows, C = max(1,
+    ceil(max_kv_len / chunk)) chunks per row (chunk = kv_chunk, or one chunk when kv_chunk <= 0),
+    regions indptr[R + 1], counts[R], o[R C][hq][64], lse[R C][hq], each on a 256-byte boundary."""
+    up = lambda x: -(-x // 256) * 256
+    R = batch * q_len
+    C = 1 if kv_chunk <= 0 else max(1, -(-max_kv_len // kv_chunk))
+    P = R * C
+    off_counts = up(4 * (R + 1))
+    off_o = off_counts + up(4 * R)
+    off_lse = off_o + up(4 * P * hq * 64)
+    return dict(rows=R, chunks=C, partials=P, off_indptr=0, off_counts=off_counts, off_o=off_o, off_lse=off_lse,
+                total=off_lse + up(4 * P * hq))
+
+
+@pytest.mark.parametrize("batch,q_len,max_kv,hq,chunk", [(64, 1, 8192, 64, 512), (32, 5, 16384, 64, 2048),
+                                                          (4, 1, 100, 8, 0), (3, 8, 1, 16, 64), (0, 1, 0, 4, 512),
+                                                          (7, 3, 4097, 12, 1024), (1, 1, 0, 1, 0)])
+def test_workspace_layout_every_offset(amd, batch, q_len, max_kv, hq, chunk):
+    got = amd.attn_sink_decode_workspace_layout(batch, q_len, max_kv, hq, 64, chunk)
+    assert got == _documented_layout(batch, q_len, max_kv, hq, chunk)
+    assert got["total"] == amd.attn_sink_decode_workspace_size(batch, q_len, max_kv, hq, 64, chunk)
+
+
+def test_workspace_layout_errors(amd):
+    with pytest.raises(amd.AttnSinkError):
+        amd.attn_sink_decode_workspace_layout(4, 1, 100, 8, 128, 512)
+    with pytest.raises(amd.AttnSinkError):
+        amd.attn_sink_decode_workspace_layout(-1, 1, 100, 8, 64, 512)
+    assert amd.lib.attn_sink_decode_workspace_layout(4, 1, 100, 8, 64, 512, None) == INVALID
+
+
 def _prefill(amd, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=None, cu_q=FAKE, cu_kv=FAKE, batch=1, total_q=16, total_kv=16,
              max_q=16, max_kv=16, hq=4, hkv=1, d=64, scale=0.125, causal=1, window=0, out=FAKE, lse=None, stream=None)
@@ -169,12 +201,12 @@ def test_decode_tree_argument_errors(amd):
 def _rope(amd, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, lens=FAKE, table=FAKE, max_pages=64, num_pages=100, kc=FAKE, vc=FAKE,
              batch=2, total_q=32, max_q=16, max_kv=1024, hq=8, hkv=2, d=64, page=16, theta=150000.0, factor=32.0,
-             orig=4096, alpha=1.0, beta=32.0, q_out=FAKE, stream=None)
+             orig=4096, alpha=1.0, beta=32.0, ramp=0, q_out=FAKE, stream=None)
     a.update(kw)
     return amd.lib.attn_sink_rope_append(a["q"], a["k"], a["v"], a["cu_q"], a["lens"], a["table"], a["max_pages"],
                                          a["num_pages"], a["kc"], a["vc"], a["batch"], a["total_q"], a["max_q"],
                                          a["max_kv"], a["hq"], a["hkv"], a["d"], a["page"], a["theta"], a["factor"],
-                                         a["orig"], a["alpha"], a["beta"], a["q_out"], a["stream"])
+                                         a["orig"], a["alpha"], a["beta"], a["ramp"], a["q_out"], a["stream"])
 
 
 def test_rope_append_argument_errors(amd):
@@ -186,6 +218,10 @@ def test_rope_append_argument_errors(amd):
     assert _rope(amd, factor=0.0) == INVALID
     assert _rope(amd, orig=0) == INVALID
     assert _rope(amd, alpha=32.0, beta=1.0) == INVALID
+    assert _rope(amd, ramp=2) == INVALID
+    assert _rope(amd, ramp=-1) == INVALID
+    assert _rope(amd, ramp=1, alpha=0.0) == INVALID           # the index ramp takes ln(r / alpha)
+    assert _rope(amd, ramp=1, batch=0) == OK
     assert _rope(amd, hq=6, hkv=4) == INVALID
     assert _rope(amd, max_pages=0) == INVALID
     for name in ("q", "k", "v", "cu_q", "lens", "table", "kc", "vc", "q_out"):

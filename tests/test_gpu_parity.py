@@ -546,7 +546,7 @@ def run_rope(amd, inp, k_new, v_new, rope=ROPE, in_place=False):
 
 def oracle_rope(inp, k_new, v_new, rope=ROPE):
     freqs, m = oracle.yarn_frequencies(64, rope["rope_theta"], rope["yarn_factor"], rope["yarn_original_len"],
-                                       rope["yarn_alpha"], rope["yarn_beta"])
+                                       rope["yarn_alpha"], rope["yarn_beta"], ramp=rope.get("yarn_ramp", "turns"))
     return oracle.rope_append(f64(inp["q"]), f64(k_new), f64(v_new), inp["cu_seqlens_q"], inp["kv_lens"],
                               inp["page_table"], f64(inp["k_cache"]), f64(inp["v_cache"]), freqs, m)
 
@@ -559,6 +559,7 @@ def assert_bf16_close(got_bits, ref, what):
 
 @pytest.mark.parametrize("hq,hkv,page_size,rope", [
     (64, 8, 16, ROPE), (8, 8, 64, ROPE), (12, 3, 256, dict(ROPE, yarn_factor=1.0)),
+    (64, 8, 16, dict(ROPE, yarn_ramp="index")), (8, 2, 32, dict(ROPE, yarn_ramp="index", yarn_alpha=2.0)),
     (16, 2, 32, dict(ROPE, rope_theta=10000.0, yarn_factor=4.0, yarn_original_len=2048))])
 def test_rope_append(amd, hq, hkv, page_size, rope):
     spec = scaled(CONFIGS["chunked_prefill"], batch=4, q_len=(1, 300), ctx_len=(0, 9000), hq=hq, hkv=hkv,

@@ -105,3 +105,77 @@ def test_append_writes_each_new_token_at_its_page_slot():
     keep = ~touched
     np.testing.assert_array_equal(np.transpose(kc, (0, 2, 1, 3))[keep], np.transpose(kc0, (0, 2, 1, 3))[keep])
     np.testing.assert_array_equal(np.transpose(vc, (0, 2, 1, 3))[keep], np.transpose(vc0, (0, 2, 1, 3))[keep])
+
+
+# ---------------------------------------------------------------------------------------
+# The ramp's interior: hand-derived values (tests/golden/yarn_ramp.json)
+# ---------------------------------------------------------------------------------------
+import json  # noqa: E402
+import os  # noqa: E402
+
+import pytest  # noqa: E402
+
+YARN_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "yarn_ramp.json")
+
+
+def _yarn_cases():
+    with open(YARN_GOLDEN) as fh:
+        data = json.load(fh)
+    return [dict(c, params=data["params"]) for c in data["cases"]]
+
+
+def _ev(expr, **names):
+    env = {"log": math.log, "exp": math.exp, "cos": math.cos, "sin": math.sin, "pi": math.pi, **names}
+    return float(eval(expr, {"__builtins__": {}}, env))
+
+
+@pytest.mark.parametrize("case", _yarn_cases(), ids=lambda c: c["name"])
+def test_yarn_ramp_interior_hand_derived(case):
+    p = case["params"]
+    i = case["pair"]
+    G = _ev(case["gamma_expr"])
+    assert math.isclose(G, case["gamma_approx"], rel_tol=5e-4, abs_tol=5e-5)
+    if "r_expr" in case:
+        assert math.isclose(_ev(case["r_expr"]), case["r_approx"], rel_tol=5e-4)
+    F = _ev(case["freq_expr"], G=G)
+    if "freq_approx" in case:
+        assert math.isclose(F, case["freq_approx"], rel_tol=5e-4)
+    f, m = oracle.yarn_frequencies(p["head_dim"], p["theta"], p["factor"], p["orig_len"], p["alpha"], p["beta"],
+                                   ramp=case["ramp"])
+    assert math.isclose(f[i], F, rel_tol=1e-12), f"pair {i}: oracle {f[i]!r}, derived {F!r}"
+    if "other_ramp_freq_expr" in case:
+        # the pin separates the two ramp forms inside the band
+        other = _ev(case["other_ramp_freq_expr"], G=G)
+        assert abs(other - F) > 0.2 * F
+        wrong = "index" if case["ramp"] == "turns" else "turns"
+        fw, _ = oracle.yarn_frequencies(p["head_dim"], p["theta"], p["factor"], p["orig_len"], p["alpha"], p["beta"],
+                                        ramp=wrong)
+        assert abs(fw[i] - F) > 0.2 * F
+    if "rotation" in case:
+        rot = case["rotation"]
+        x = np.zeros((1, 1, p["head_dim"]))
+        x[0, 0, i], x[0, 0, i + p["head_dim"] // 2] = rot["x_pair"]
+        y = oracle.rotate(x, np.array([rot["position"]]), f, m)
+        exp_lo, exp_hi = (_ev(e, F=F) for e in rot["expect_expr"])
+        assert math.isclose(y[0, 0, i], exp_lo, rel_tol=1e-9, abs_tol=1e-12)
+        assert math.isclose(y[0, 0, i + p["head_dim"] // 2], exp_hi, rel_tol=1e-9, abs_tol=1e-12)
+        others = np.delete(y[0, 0], [i, i + p["head_dim"] // 2])
+        assert np.all(others == 0.0)
+
+
+def test_yarn_index_ramp_is_linear_in_the_pair_index():
+    """Inside the band the 'index' form's weight falls by the same step from pair to pair, and
+    its ends sit where r = beta and r = alpha."""
+    theta, s, L0, a, b = 150000.0, 32.0, 4096, 1.0, 32.0
+    f, _ = oracle.yarn_frequencies(64, theta, s, L0, a, b, ramp="index")
+    base, _ = oracle.yarn_frequencies(64, theta, 1.0, L0, a, b)
+    g = (f / base - 1.0 / s) / (1.0 - 1.0 / s)
+    inside = np.flatnonzero((g > 0) & (g < 1))
+    assert len(inside) >= 5
+    steps = np.diff(g[inside])
+    np.testing.assert_allclose(steps, steps[0], rtol=1e-9)
+    i_beta = 32 * math.log(L0 / (2 * math.pi * b)) / math.log(theta)
+    i_alpha = 32 * math.log(L0 / (2 * math.pi * a)) / math.log(theta)
+    assert math.isclose(steps[0], -1.0 / (i_alpha - i_beta), rel_tol=1e-9)
+    with pytest.raises(ValueError):
+        oracle.yarn_frequencies(64, theta, s, L0, a, b, ramp="linear")
