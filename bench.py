@@ -324,7 +324,7 @@ def bench_paged(args, torch, amd, name):
                                             spec.causal, spec.window, spec.kv_chunk, workspace=ws)
     split_ms = None if tree else time_calls(torch, split_only, args.steps, args.warmup)
     # merge kernel alone on the same partials
-    lay = amd.decode_workspace_layout(B, ql, inp["max_kv_len"], hq, spec.kv_chunk, spec.page_size)
+    lay = amd.decode_workspace_layout(B, ql, inp["max_kv_len"], hq, spec.kv_chunk)
     n_p = lay["partials"]
     o_p = ws[lay["off_o"]:lay["off_o"] + 4 * n_p * hq * 64].view(torch.float32).view(n_p, hq, 64)
     l_p = ws[lay["off_lse"]:lay["off_lse"] + 4 * n_p * hq].view(torch.float32).view(n_p, hq)

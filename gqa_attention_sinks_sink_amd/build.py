@@ -18,8 +18,6 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libattnsink.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-# Developer override: load a library built elsewhere (e.g. an experimental variant).
-LIB_LOAD_PATH = os.environ.get("ATTN_SINK_LIB", LIB_PATH)
 SOURCES = ["api.hip", "prefill.hip", "decode.hip", "merge.hip", "rope.hip"]
 ARCH = "gfx950"
 
