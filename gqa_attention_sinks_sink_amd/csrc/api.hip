@@ -287,15 +287,26 @@ attn_sink_status attn_sink_decode_workspace_layout(int32_t batch, int32_t q_len,
 }  // extern "C"
 
 namespace {
+// Points the plan and partial arrays of p into a workspace laid out as lay.
+void bind_workspace(DecodeParams* pp, const DecodeLayout& lay, void* workspace) {
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  pp->indptr = reinterpret_cast<int32_t*>(ws + lay.off_indptr);
+  pp->counts = reinterpret_cast<int32_t*>(ws + lay.off_counts);
+  pp->o_part = reinterpret_cast<float*>(ws + lay.off_o);
+  pp->lse_part = reinterpret_cast<float*>(ws + lay.off_lse);
+}
+
 // Validation and parameters shared by the decode entry points. out_required: the call also
-// merges (out must be given).
+// merges (out must be given). caller_workspace: the workspace pointer comes from the caller
+// (checked for NULL and alignment here, and bound into *pp); otherwise the caller of this
+// function binds the library's own scratch after validation, and workspace is unused.
 attn_sink_status decode_prepare(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
                                 int32_t max_pages_per_seq, int32_t num_pages, const int32_t* kv_lens,
                                 const float* sinks, int32_t batch, int32_t q_len, int32_t max_kv_len,
                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                                 float softmax_scale, int32_t causal, int32_t window, int32_t kv_chunk,
-                                void* workspace, size_t workspace_bytes, const void* out, bool out_required,
-                                DecodeParams* pp, DecodeLayout* lp) {
+                                void* workspace, size_t workspace_bytes, bool caller_workspace, const void* out,
+                                bool out_required, DecodeParams* pp, DecodeLayout* lp) {
   if (batch < 0 || max_kv_len < 0 || max_pages_per_seq < 1 || num_pages < 1 || q_len < 1) return ATTN_SINK_ERR_INVALID_ARG;
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return ATTN_SINK_ERR_INVALID_ARG;
   if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_SINK_ERR_INVALID_ARG;
@@ -313,16 +324,15 @@ attn_sink_status decode_prepare(const void* q, const void* k_cache, const void* 
   *lp = lay;
   if (batch == 0) return ATTN_SINK_OK;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || page_table == nullptr || kv_lens == nullptr ||
-      (out_required && out == nullptr) || workspace == nullptr)
+      (out_required && out == nullptr) || (caller_workspace && workspace == nullptr))
     return ATTN_SINK_ERR_INVALID_ARG;
   if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache) || (out != nullptr && misaligned16(out)))
     return ATTN_SINK_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_SINK_ERR_INVALID_ARG;
+  if (caller_workspace && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_SINK_ERR_INVALID_ARG;
   if (workspace_bytes < attn_sink_decode_workspace_size(batch, q_len, max_kv_len, num_q_heads, head_dim, kv_chunk) ||
       workspace_bytes < lay.total)
     return ATTN_SINK_ERR_WORKSPACE_TOO_SMALL;
 
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
   DecodeParams& p = *pp;
   p.q = static_cast<const uint16_t*>(q);
   p.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -330,10 +340,7 @@ attn_sink_status decode_prepare(const void* q, const void* k_cache, const void* 
   p.page_table = page_table;
   p.kv_lens = kv_lens;
   p.sinks = sinks;
-  p.indptr = reinterpret_cast<int32_t*>(ws + lay.off_indptr);
-  p.counts = reinterpret_cast<int32_t*>(ws + lay.off_counts);
-  p.o_part = reinterpret_cast<float*>(ws + lay.off_o);
-  p.lse_part = reinterpret_cast<float*>(ws + lay.off_lse);
+  if (caller_workspace) bind_workspace(&p, lay, workspace);
   p.batch = batch;
   p.q_len = q_len;
   p.max_kv_len = max_kv_len;
@@ -351,6 +358,22 @@ attn_sink_status decode_prepare(const void* q, const void* k_cache, const void* 
   p.tree_mask = nullptr;
   return ATTN_SINK_OK;
 }
+
+// The split-KV kernel, then the merge of its partials into out / lse.
+attn_sink_status decode_split_and_merge(const DecodeParams& p, const DecodeLayout& lay, void* out, float* lse,
+                                        hipStream_t s) {
+  if (launch_decode_split(p, (int)lay.chunks, s) != hipSuccess) return ATTN_SINK_ERR_HIP;
+  MergeParams mp;
+  mp.o_part = p.o_part;
+  mp.lse_part = p.lse_part;
+  mp.indptr = p.indptr;
+  mp.out = static_cast<uint16_t*>(out);
+  mp.lse = lse;
+  mp.num_partials = (int)lay.partials;
+  mp.rows = (int)lay.rows;
+  mp.hq = p.hq;
+  return hip_status(launch_merge(mp, s));
+}
 }  // namespace
 
 extern "C" {
@@ -367,22 +390,9 @@ attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, cons
   const attn_sink_status st = decode_prepare(q, k_cache, v_cache, page_table, max_pages_per_seq, num_pages, kv_lens,
                                              sinks, batch, q_len, max_kv_len, num_q_heads, num_kv_heads, head_dim,
                                              page_size, softmax_scale, causal, window, kv_chunk, workspace,
-                                             workspace_bytes, out, true, &p, &lay);
+                                             workspace_bytes, true, out, true, &p, &lay);
   if (st != ATTN_SINK_OK || batch == 0) return st;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_decode_split(p, (int)lay.chunks, s);
-  if (e != hipSuccess) return ATTN_SINK_ERR_HIP;
-
-  MergeParams mp;
-  mp.o_part = p.o_part;
-  mp.lse_part = p.lse_part;
-  mp.indptr = p.indptr;
-  mp.out = static_cast<uint16_t*>(out);
-  mp.lse = lse;
-  mp.num_partials = (int)lay.partials;
-  mp.rows = (int)lay.rows;
-  mp.hq = num_q_heads;
-  return hip_status(launch_merge(mp, s));
+  return decode_split_and_merge(p, lay, out, lse, reinterpret_cast<hipStream_t>(stream));
 }
 
 attn_sink_status attn_sink_decode_paged_tree(const void* q, const void* k_cache, const void* v_cache,
@@ -397,24 +407,11 @@ attn_sink_status attn_sink_decode_paged_tree(const void* q, const void* k_cache,
   const attn_sink_status st = decode_prepare(q, k_cache, v_cache, page_table, max_pages_per_seq, num_pages, kv_lens,
                                              sinks, batch, q_len, max_kv_len, num_q_heads, num_kv_heads, head_dim,
                                              page_size, softmax_scale, 1, window, kv_chunk, workspace,
-                                             workspace_bytes, out, true, &p, &lay);
+                                             workspace_bytes, true, out, true, &p, &lay);
   if (st != ATTN_SINK_OK || batch == 0) return st;
   if (tree_mask == nullptr) return ATTN_SINK_ERR_INVALID_ARG;
   p.tree_mask = tree_mask;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_decode_split(p, (int)lay.chunks, s);
-  if (e != hipSuccess) return ATTN_SINK_ERR_HIP;
-
-  MergeParams mp;
-  mp.o_part = p.o_part;
-  mp.lse_part = p.lse_part;
-  mp.indptr = p.indptr;
-  mp.out = static_cast<uint16_t*>(out);
-  mp.lse = lse;
-  mp.num_partials = (int)lay.partials;
-  mp.rows = (int)lay.rows;
-  mp.hq = num_q_heads;
-  return hip_status(launch_merge(mp, s));
+  return decode_split_and_merge(p, lay, out, lse, reinterpret_cast<hipStream_t>(stream));
 }
 
 attn_sink_status attn_sink_decode_paged_partials(const void* q, const void* k_cache, const void* v_cache,
@@ -430,7 +427,7 @@ attn_sink_status attn_sink_decode_paged_partials(const void* q, const void* k_ca
   const attn_sink_status st = decode_prepare(q, k_cache, v_cache, page_table, max_pages_per_seq, num_pages, kv_lens,
                                              sinks, batch, q_len, max_kv_len, num_q_heads, num_kv_heads, head_dim,
                                              page_size, softmax_scale, causal, window, kv_chunk, workspace,
-                                             workspace_bytes, nullptr, false, &p, &lay);
+                                             workspace_bytes, true, nullptr, false, &p, &lay);
   if (st != ATTN_SINK_OK || batch == 0) return st;
   return hip_status(launch_decode_split(p, (int)lay.chunks, reinterpret_cast<hipStream_t>(stream)));
 }
