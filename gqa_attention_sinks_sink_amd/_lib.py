@@ -22,14 +22,16 @@ __all__ = [
     "attn_sink_decode_paged_partials", "attn_sink_decode_paged_tree", "attn_sink_rope_append",
     "attn_sink_decode_workspace_size",
     "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version", "decode_workspace_layout",
-    "attn_sink_decode_workspace_layout", "EXPORTED_SYMBOLS",
+    "attn_sink_decode_workspace_layout", "attn_sink_decode_paged_noalloc", "attn_sink_decode_noalloc_capacity",
+    "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
     "attn_sink_prefill", "attn_sink_prefill_paged", "attn_sink_decode_paged", "attn_sink_decode_paged_partials",
     "attn_sink_decode_paged_tree", "attn_sink_rope_append",
     "attn_sink_decode_workspace_size", "attn_sink_decode_workspace_layout", "attn_sink_merge_partials",
-    "attn_sink_status_string", "attn_sink_version",
+    "attn_sink_status_string", "attn_sink_version", "attn_sink_decode_paged_noalloc",
+    "attn_sink_decode_noalloc_capacity",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -59,6 +61,11 @@ lib.attn_sink_decode_paged.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp,
 lib.attn_sink_decode_paged_partials.restype = ctypes.c_int
 lib.attn_sink_decode_paged_partials.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _i32, _i32, _i32, _i32,
                                                 _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz, _vp]
+lib.attn_sink_decode_paged_noalloc.restype = ctypes.c_int
+lib.attn_sink_decode_paged_noalloc.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _i32, _i32, _i32, _i32, _i32,
+                                               _i32, _i32, _f32, _i32, _i32, _i32, _vp, _fp, _vp]
+lib.attn_sink_decode_noalloc_capacity.restype = _sz
+lib.attn_sink_decode_noalloc_capacity.argtypes = []
 lib.attn_sink_decode_workspace_size.restype = _sz
 lib.attn_sink_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 lib.attn_sink_decode_workspace_layout.restype = ctypes.c_int
@@ -331,6 +338,55 @@ def attn_sink_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                     _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
                                     _ptr(lse), _stream(stream))
     _raise(st, "attn_sink_decode_paged")
+    return out, lse
+
+
+def attn_sink_decode_noalloc_capacity() -> int:
+    return int(lib.attn_sink_decode_noalloc_capacity())
+
+
+def attn_sink_decode_paged_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   page_table: torch.Tensor, kv_lens: torch.Tensor, sinks: Optional[torch.Tensor],
+                                   q_len: int, max_kv_len: int, softmax_scale: Optional[float] = None,
+                                   causal: bool = True, window: int = 0, kv_chunk: int = 512,
+                                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """attn_sink_decode_paged with the library's own scratch in place of a workspace. The caller passes out
+    (and lse, or None): this function allocates nothing."""
+    dev = q.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check(t, n, torch.bfloat16, dev)
+    _check(page_table, "page_table", torch.int32, dev)
+    _check(kv_lens, "kv_lens", torch.int32, dev)
+    if sinks is not None:
+        _check(sinks, "sinks", torch.float32, dev)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape or k_cache.shape[3] != q.shape[2]:
+        raise ValueError(f"expected q [rows, hq, d] and caches [pages, hkv, page_size, d]; got {tuple(q.shape)}, "
+                         f"{tuple(k_cache.shape)}, {tuple(v_cache.shape)}")
+    rows, hq, d = q.shape
+    batch = kv_lens.numel()
+    if rows != batch * q_len:
+        raise ValueError(f"q has {rows} rows, expected batch*q_len = {batch * q_len}")
+    if page_table.dim() != 2 or page_table.shape[0] != batch:
+        raise ValueError(f"page_table must be [{batch}, max_pages_per_seq]")
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    _check(out, "out", torch.bfloat16, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, dev)
+        if lse.shape != (rows, hq):
+            raise ValueError(f"lse must be [{rows}, {hq}]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    num_pages, hkv, page_size = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    st = lib.attn_sink_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                            page_table.shape[1], num_pages, _ptr(kv_lens), _ptr(sinks), batch, q_len,
+                                            int(max_kv_len), hq, hkv, d, page_size, float(softmax_scale),
+                                            int(bool(causal)), int(window), int(kv_chunk), _ptr(out), _ptr(lse),
+                                            _stream(stream))
+    _raise(st, "attn_sink_decode_paged_noalloc")
     return out, lse
 
 

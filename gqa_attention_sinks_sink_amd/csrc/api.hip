@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/attn_sink.h"
 #include "common.hpp"
@@ -62,6 +63,39 @@ inline bool decode_layout(int32_t batch, int32_t q_len, int32_t max_kv_len, int3
   l.total = l.off_lse + align256(sizeof(float) * (size_t)l.partials * num_q_heads);
   *out = l;
   return true;
+}
+
+// Scratch of attn_sink_decode_paged_noalloc (the plan and the chunk partials of one call), in
+// device memory the library owns: each GPU the library runs on holds its own copy until the
+// process ends. Host code never uses the array's name as an address: the device address comes
+// from hipGetSymbolAddress, once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on the first call on that device).
+hipError_t current_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&]() {
+    void* ptr = nullptr;
+    slot.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (slot.err == hipSuccess && ptr == nullptr) slot.err = hipErrorInvalidSymbol;
+    slot.ptr = ptr;
+  });
+  if (slot.err != hipSuccess) return slot.err;
+  *out = slot.ptr;
+  return hipSuccess;
 }
 
 // Launchers return hipErrorInvalidConfiguration for a grid beyond the launch limits.
@@ -394,6 +428,31 @@ attn_sink_status attn_sink_decode_paged(const void* q, const void* k_cache, cons
   if (st != ATTN_SINK_OK || batch == 0) return st;
   return decode_split_and_merge(p, lay, out, lse, reinterpret_cast<hipStream_t>(stream));
 }
+
+attn_sink_status attn_sink_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                                const int32_t* page_table, int32_t max_pages_per_seq,
+                                                int32_t num_pages, const int32_t* kv_lens, const float* sinks,
+                                                int32_t batch, int32_t q_len, int32_t max_kv_len,
+                                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t page_size, float softmax_scale, int32_t causal,
+                                                int32_t window, int32_t kv_chunk, void* out, float* lse,
+                                                void* stream) {
+  DecodeParams p{};
+  DecodeLayout lay;
+  // Everything is validated (the layout against the scratch's size included) before the first
+  // HIP call.
+  const attn_sink_status st = decode_prepare(q, k_cache, v_cache, page_table, max_pages_per_seq, num_pages, kv_lens,
+                                             sinks, batch, q_len, max_kv_len, num_q_heads, num_kv_heads, head_dim,
+                                             page_size, softmax_scale, causal, window, kv_chunk, nullptr,
+                                             kNoAllocScratchBytes, false, out, true, &p, &lay);
+  if (st != ATTN_SINK_OK || batch == 0) return st;
+  void* ws = nullptr;
+  if (current_scratch(&ws) != hipSuccess) return ATTN_SINK_ERR_HIP;
+  bind_workspace(&p, lay, ws);
+  return decode_split_and_merge(p, lay, out, lse, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t attn_sink_decode_noalloc_capacity(void) { return kNoAllocScratchBytes; }
 
 attn_sink_status attn_sink_decode_paged_tree(const void* q, const void* k_cache, const void* v_cache,
                                              const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,

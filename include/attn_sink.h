@@ -235,6 +235,36 @@ attn_sink_status attn_sink_rope_append(
     int32_t yarn_ramp, void* q_out, void* stream);
 
 /*
+ * attn_sink_decode_paged without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The plan and the chunk partials go to a scratch array inside the library
+ * (attn_sink_decode_noalloc_capacity() bytes, 64 MiB: e.g. 64 sequences of up to 8192 keys at
+ * q_len 1 in 512-token chunks need 16.3 MiB, 32 sequences of up to 16384 keys at q_len 5 in
+ * 2048-token chunks 20.3 MiB); each GPU the library runs on holds its own copy from the first
+ * call on it until the process ends. The call allocates nothing and calls no allocating
+ * routine. The same kernels run as for attn_sink_decode_paged, with the same results.
+ *
+ * Arguments, constraints and error codes as for attn_sink_decode_paged without workspace and
+ * workspace_bytes; a call whose workspace (attn_sink_decode_workspace_size of its scalars)
+ * exceeds the capacity returns ATTN_SINK_ERR_WORKSPACE_TOO_SMALL with nothing launched. Every
+ * call on one GPU uses that GPU's one scratch array: calls that may run at the same time on
+ * one GPU (different streams, or different host threads) race on it and must be ordered by
+ * the caller. The scratch keeps the last call's plan and partials; nothing in it needs to
+ * start at zero. Enqueues two kernels (split-KV chunks, then the merge).
+ */
+attn_sink_status attn_sink_decode_paged_noalloc(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    const int32_t* kv_lens, const float* sinks,
+    int32_t batch, int32_t q_len, int32_t max_kv_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    float softmax_scale, int32_t causal, int32_t window, int32_t kv_chunk,
+    void* out, float* lse, void* stream);
+
+/* Bytes of scratch attn_sink_decode_paged_noalloc can use on each GPU (a constant). */
+size_t attn_sink_decode_noalloc_capacity(void);
+
+/*
  * Verification of a draft tree in one step ("Accelerating Sonar through speculation", EAGLE
  * section: tree-shaped drafts need a custom attention mask, which a full-sequence mask made
  * costly). The mask is a bitmap per draft row: the q_len draft tokens are the last q_len of

@@ -317,3 +317,34 @@ def test_binding_refuses_cpu_tensors(amd):
     cu = torch.tensor([0, 16], dtype=torch.int32)
     with pytest.raises((TypeError, ValueError, RuntimeError)):
         amd.attn_sink_prefill(q.float(), q, q, None, cu, cu, 16, 16)
+
+
+def _noalloc(amd, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, table=FAKE, max_pages=64, num_pages=100, lens=FAKE, sinks=None, batch=4,
+             q_len=1, max_kv=1024, hq=16, hkv=2, d=64, page=16, scale=0.125, causal=1, window=0, chunk=512, out=FAKE,
+             lse=None, stream=None)
+    a.update(kw)
+    return amd.lib.attn_sink_decode_paged_noalloc(a["q"], a["kc"], a["vc"], a["table"], a["max_pages"],
+                                                  a["num_pages"], a["lens"], a["sinks"], a["batch"], a["q_len"],
+                                                  a["max_kv"], a["hq"], a["hkv"], a["d"], a["page"], a["scale"],
+                                                  a["causal"], a["window"], a["chunk"], a["out"], a["lse"],
+                                                  a["stream"])
+
+
+def test_decode_noalloc_argument_errors(amd):
+    """Every rejection happens on the host, before the scratch is looked up or anything launched."""
+    cap = amd.attn_sink_decode_noalloc_capacity()
+    assert cap == 64 << 20
+    assert _noalloc(amd, d=128) == UNSUPPORTED
+    assert _noalloc(amd, q_len=9) == UNSUPPORTED
+    assert _noalloc(amd, chunk=100) == UNSUPPORTED
+    assert _noalloc(amd, scale=0.0) == INVALID
+    assert _noalloc(amd, out=None) == INVALID
+    for name in ("q", "kc", "vc", "table", "lens"):
+        assert _noalloc(amd, **{name: None}) == INVALID, name
+    assert _noalloc(amd, q=FAKE + 8) == INVALID
+    # beyond the scratch: the workspace these scalars need exceeds the capacity
+    big = dict(batch=64, q_len=8, max_kv=131072, hq=64, hkv=8, chunk=64, max_pages=8192)
+    assert amd.attn_sink_decode_workspace_size(64, 8, 131072, 64, 64, 64) > cap
+    assert _noalloc(amd, **big) == WS_SMALL
+    assert _noalloc(amd, batch=0) == OK
