@@ -23,7 +23,7 @@ __all__ = [
     "attn_sink_decode_workspace_size",
     "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version", "decode_workspace_layout",
     "attn_sink_decode_workspace_layout", "attn_sink_decode_paged_noalloc", "attn_sink_decode_noalloc_capacity",
-    "EXPORTED_SYMBOLS",
+    "attn_sink_decode_paged_tree_partials", "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "attn_sink_decode_paged_tree", "attn_sink_rope_append",
     "attn_sink_decode_workspace_size", "attn_sink_decode_workspace_layout", "attn_sink_merge_partials",
     "attn_sink_status_string", "attn_sink_version", "attn_sink_decode_paged_noalloc",
-    "attn_sink_decode_noalloc_capacity",
+    "attn_sink_decode_noalloc_capacity", "attn_sink_decode_paged_tree_partials",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -66,6 +66,9 @@ lib.attn_sink_decode_paged_noalloc.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _
                                                _i32, _i32, _f32, _i32, _i32, _i32, _vp, _fp, _vp]
 lib.attn_sink_decode_noalloc_capacity.restype = _sz
 lib.attn_sink_decode_noalloc_capacity.argtypes = []
+lib.attn_sink_decode_paged_tree_partials.restype = ctypes.c_int
+lib.attn_sink_decode_paged_tree_partials.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _fp, _i32, _i32, _i32,
+                                                     _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]
 lib.attn_sink_decode_workspace_size.restype = _sz
 lib.attn_sink_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 lib.attn_sink_decode_workspace_layout.restype = ctypes.c_int
@@ -448,16 +451,45 @@ def attn_sink_decode_paged_partials(q: torch.Tensor, k_cache: torch.Tensor, v_ca
                                              int(bool(causal)), int(window), int(kv_chunk), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream))
     _raise(st, "attn_sink_decode_paged_partials")
-    lay = attn_sink_decode_workspace_layout(batch, q_len, int(max_kv_len), hq, d, kv_chunk)
+    return _partial_views(workspace, batch, q_len, int(max_kv_len), hq, d, kv_chunk)
+
+
+def _partial_views(workspace, batch, q_len, max_kv_len, hq, d, kv_chunk) -> dict:
+    lay = attn_sink_decode_workspace_layout(batch, q_len, max_kv_len, hq, d, kv_chunk)
     ws = workspace.view(torch.uint8).reshape(-1)
-    n_p = lay["partials"]
+    rows, n_p = batch * q_len, lay["partials"]
     return dict(
         workspace=workspace,
-        partial_indptr=ws[:4 * (rows + 1)].view(torch.int32),
+        partial_indptr=ws[lay["off_indptr"]:lay["off_indptr"] + 4 * (rows + 1)].view(torch.int32),
         chunk_counts=ws[lay["off_counts"]:lay["off_counts"] + 4 * rows].view(torch.int32),
         o_partial=ws[lay["off_o"]:lay["off_o"] + 4 * n_p * hq * d].view(torch.float32).view(n_p, hq, d),
         lse_partial=ws[lay["off_lse"]:lay["off_lse"] + 4 * n_p * hq].view(torch.float32).view(n_p, hq),
     )
+
+
+def attn_sink_decode_paged_tree_partials(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                         page_table: torch.Tensor, kv_lens: torch.Tensor, tree_mask: torch.Tensor,
+                                         sinks: Optional[torch.Tensor], q_len: int, max_kv_len: int,
+                                         softmax_scale: Optional[float] = None, window: int = 0,
+                                         kv_chunk: int = 512, workspace: Optional[torch.Tensor] = None,
+                                         stream=None) -> dict:
+    """The split-KV pass of attn_sink_decode_paged_tree alone; returns the same views as
+    attn_sink_decode_paged_partials."""
+    batch, rows, hq, d, workspace = _decode_args(q, k_cache, v_cache, page_table, kv_lens, sinks, q_len, workspace,
+                                                 kv_chunk, max_kv_len)
+    _check(tree_mask, "tree_mask", torch.int32, q.device)
+    if tree_mask.numel() != rows:
+        raise ValueError(f"tree_mask must have batch * q_len = {rows} entries")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    num_pages, hkv, page_size = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    st = lib.attn_sink_decode_paged_tree_partials(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                                  page_table.shape[1], num_pages, _ptr(kv_lens), _ptr(tree_mask),
+                                                  _ptr(sinks), batch, q_len, int(max_kv_len), hq, hkv, d, page_size,
+                                                  float(softmax_scale), int(window), int(kv_chunk), _ptr(workspace),
+                                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise(st, "attn_sink_decode_paged_tree_partials")
+    return _partial_views(workspace, batch, q_len, int(max_kv_len), hq, d, kv_chunk)
 
 
 def attn_sink_merge_partials(o_partial: torch.Tensor, lse_partial: torch.Tensor, partial_indptr: torch.Tensor,

@@ -305,6 +305,21 @@ attn_sink_status attn_sink_decode_paged_partials(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The split-KV pass of attn_sink_decode_paged_tree alone (the tree counterpart of
+ * attn_sink_decode_paged_partials): plan and chunk partials in the workspace, no merge.
+ * Arguments, constraints and error codes as for attn_sink_decode_paged_tree, without out and
+ * lse. Enqueues one kernel.
+ */
+attn_sink_status attn_sink_decode_paged_tree_partials(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    const int32_t* kv_lens, const int32_t* tree_mask, const float* sinks,
+    int32_t batch, int32_t q_len, int32_t max_kv_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    float softmax_scale, int32_t window, int32_t kv_chunk,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of workspace attn_sink_decode_paged needs for these host scalars (0 if they are
  * invalid). Monotone non-decreasing in batch, q_len, max_kv_len and num_q_heads.
  */

@@ -505,6 +505,25 @@ def test_tree_chain_is_bit_identical_to_causal_verify(amd):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_tree_partials_then_merge_equals_tree_call(amd):
+    """The tree split-only entry point followed by attn_sink_merge_partials reproduces
+    attn_sink_decode_paged_tree bit for bit (the same kernels run); the plan matches the oracle's."""
+    spec = scaled(CONFIGS["tree_verify"], batch=5, kv_len=(8, 1700), hq=16, hkv=2, kv_chunk=256, seed=96)
+    inp = make_paged(spec)
+    d = dev_paged(inp)
+    trees = make_tree_masks(spec)
+    out, lse = run_tree(amd, d, inp, spec, trees)
+    parts = amd.attn_sink_decode_paged_tree_partials(d["q"], d["k"], d["v"], d["table"], d["lens"],
+                                                     torch.from_numpy(trees).to(DEV), d["sinks"], spec.q_len,
+                                                     inp["max_kv_len"], spec.scale, spec.window, spec.kv_chunk)
+    out2, lse2 = amd.attn_sink_merge_partials(parts["o_partial"], parts["lse_partial"], parts["partial_indptr"])
+    torch.cuda.synchronize()
+    assert np.array_equal(out_f64(out2), out) and np.array_equal(lse2.cpu().numpy().astype(np.float64), lse)
+    exp_counts, exp_indptr = oracle.plan_chunks(inp["kv_lens"], spec.q_len, spec.kv_chunk)
+    assert parts["chunk_counts"].cpu().numpy().tolist() == exp_counts
+    assert parts["partial_indptr"].cpu().numpy().tolist() == exp_indptr
+
+
 def test_tree_edge_bitmaps(amd):
     # empty bitmaps (prefix only), all bits (every draft token), bits past q_len (ignored),
     # sequences no longer than the draft block
