@@ -1,24 +1,34 @@
 """Benchmark of the sink-attention hot path on one MI355X.
 
-Default workload: paged split-KV decode (64 sequences, q_len 1, KV lengths uniform in
-[1024, 8192], 64 query / 8 KV heads, head_dim 64, bf16, 16-token pages in a seeded random
-order, 512-token chunks merged by log-sum-exp). One step = one attn_sink_decode_paged call
-(split-KV kernel + merge kernel) over the whole batch, inputs resident in HBM.
+Default run: the two halves of the headline metric on one line.
+  * paged decode (top level): 64 sequences, q_len 1, KV lengths uniform in [1024, 8192],
+    64 query / 8 KV heads, head_dim 64, bf16, 16-token pages in a seeded random order,
+    512-token chunks merged by log-sum-exp. One step = one attn_sink_decode_paged call
+    (split-KV kernel + merge kernel) over the whole batch; HBM GB/s.
+  * causal prefill (the "prefill" object): 8 x 4096 tokens packed, 64 query / 8 KV heads;
+    one step = one attn_sink_prefill call; TFLOP/s against the bf16 MFMA peak.
+Other workloads (--workload): verify, tree_verify, window_prefill, embed (two passes: sinks
+disabled, then N(0,1) sinks), chunked_prefill, rope_append, tiny_causal, and each half alone.
 
-Other workloads (--workload): causal_prefill, window_prefill, verify, embed (two passes:
-sinks disabled, then N(0,1) sinks), chunked_prefill (2048-token chunks appended to paged
-caches of 0..6144 tokens), tree_verify (8-node draft trees per sequence, one-step
-verification), rope_append (YaRN rotary encoding of the chunked-prefill workload's 16384 new
-tokens and the append of their K/V into the paged cache), tiny_causal.
-
-Prints ONE JSON line. ``value`` is the algorithmic rate of the whole step (GB/s for the
-memory-bound paths, TFLOP/s for prefill); ``roofline`` describes the dominant kernel, timed
-with HIP events on the stream it runs on; ``cpu_baseline`` times the fp64 CPU oracle on a
-bounded sample of the same workload (rank 0, N=1 only).
+Every timed call is first checked against the fp64 CPU oracle on sampled rows (the accuracy
+gate comes before any timing); a mismatch exits with status 3 and no timing line. Then:
+  * value: the whole step, W eager warmup steps, then exactly K steps captured in a HIP graph
+    and replayed between two HIP events on the launch stream, inputs resident in HBM;
+  * cold_*: the median of single calls each preceded by a 1 GiB read that flushes the L2 and
+    the MALL (the flush is outside the timed region);
+  * roofline: the dominant kernel's algorithmic bytes (or FLOPs) per launch over its average
+    launch time, measured the same way (decode: the split-only entry point);
+  * cpu_baseline: the fp64 oracle, unchanged, run before the GPU is touched, by a pool of
+    worker processes on the host's cores (at most 16), each with BLAS on one thread, over a
+    bounded sample of the same workload.
+Prints ONE JSON line. --record-traffic and --summarize turn rocprofv3 outputs into the
+summaries under profiles/ (host only).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -30,17 +40,21 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import (CONFIGS, bf16_bits_to_f32, make_paged, make_paged_prefill, make_tree_masks,  # noqa: E402
-                       make_varlen)
+from workloads import (CONFIGS, bf16_bits_to_f32, bf16_round_bits, make_paged, make_paged_prefill,  # noqa: E402
+                       make_tree_masks, make_varlen)
 
 METRIC = "sink-attn decode HBM GB/s (% peak); prefill TFLOP/s (% bf16 MFMA peak)"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
+ATOL, RTOL, LSE_TOL = 1e-2, 1e-2, 1e-3
 KERNEL_SOURCES = {
     "rope": ["rope.hip", "common.hpp", "kernels.hpp"],
     "decode": ["decode.hip", "common.hpp", "kernels.hpp"],
     "prefill": ["prefill.hip", "common.hpp", "kernels.hpp"],
 }
+WORKLOADS = ["default", "paged_decode", "verify", "tree_verify", "causal_prefill", "window_prefill", "embed",
+             "chunked_prefill", "rope_append", "tiny_causal"]
+ROPE_ARGS = dict(rope_theta=150000.0, yarn_factor=32.0, yarn_original_len=4096, yarn_alpha=1.0, yarn_beta=32.0)
 
 
 def parse():
@@ -48,12 +62,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="paged_decode",
-                    choices=["paged_decode", "verify", "tree_verify", "causal_prefill", "window_prefill", "embed",
-                             "chunked_prefill", "rope_append", "tiny_causal"])
+    ap.add_argument("--workload", default="default", choices=WORKLOADS,
+                    help="default: paged decode with causal prefill as its 'prefill' object")
     ap.add_argument("--kv-chunk", type=int, default=None,
                     help="split-KV chunk length for the paged workloads (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU oracle sample (wall seconds)")
+    ap.add_argument("--cpu-workers", type=int, default=None,
+                    help="oracle worker processes (default: the host cores this process may use, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache timing (profiling runs: every call is then a warm, timed one)")
@@ -62,11 +77,34 @@ def parse():
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs (workload, then the plain copy) into "
                          "profiles/traffic.json for --workload; runs on the host only")
+    ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "OUT_MD", "TITLE"),
+                    help="write a markdown summary of a rocprofv3 --stats output (kernel_stats.csv) to OUT_MD; "
+                         "--summary-command names the command that produced it; runs on the host only")
+    ap.add_argument("--summary-command", default="", help="the command recorded in a --summarize summary")
     return ap.parse_args()
 
 
-def tbits(torch, bits, dev):
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+# ------------------------------------------------------------------------------------------
+# host-side helpers
+# ------------------------------------------------------------------------------------------
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers(args):
+    n = len(os.sched_getaffinity(0))
+    return max(1, min(n, 16) if args.cpu_workers is None else args.cpu_workers)
+
+
+def f64(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
 
 
 def source_hash(kind):
@@ -93,8 +131,6 @@ def measured_traffic(name, kind):
 
 def _pmc_per_dispatch(directory, counter):
     """{dispatch id: (kernel name, value)} for one counter of a rocprofv3 --pmc CSV output."""
-    import csv
-    import glob
     vals = {}
     for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as fh:
@@ -107,25 +143,30 @@ def _pmc_per_dispatch(directory, counter):
     return vals
 
 
-def prefill_kernel_name(spec, max_seqlen):
+def prefill_kernel_name(window, max_seqlen):
     """The prefill kernel the library launches for this shape (8-wave ping-pong kernel for
-    sequences of 2048+ tokens without a window, else the 4-wave kernel)."""
-    return "prefill_pp_kernel" if (spec.window <= 0 and max_seqlen >= 2048) else "prefill_kernel"
+    query ranges of 2048+ tokens without a window, else the 4-wave kernel)."""
+    return "prefill_pp_kernel" if (window <= 0 and max_seqlen >= 2048) else "prefill_kernel"
 
 
 def dominant_kernel(name):
-    if name in ("paged_decode", "verify", "tree_verify"):
+    if name in ("paged_decode", "verify", "tree_verify", "default"):
         return "decode_split_kernel"
     if name == "rope_append":
         return "rope_append_kernel"
     if name == "chunked_prefill":
         spec = CONFIGS[name]
-        return "prefill_pp_kernel" if (spec.window <= 0 and spec.q_len[1] >= 2048) else "prefill_kernel"
+        return prefill_kernel_name(spec.window, spec.q_len[1])
     spec = CONFIGS["embed_sink" if name == "embed" else name]
-    return prefill_kernel_name(spec, spec.seqlen[1])
+    return prefill_kernel_name(spec.window, spec.seqlen[1])
 
 
-def record_traffic(name, kind, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+def kernel_kind(name):
+    return ("decode" if name in ("paged_decode", "verify", "tree_verify", "default") else
+            "rope" if name == "rope_append" else "prefill")
+
+
+def record_traffic(name, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     """HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB
     per dispatch), each scaled so that a plain 1 GiB device copy reads and writes 1 GiB."""
     kernel = dominant_kernel(name)
@@ -138,8 +179,7 @@ def record_traffic(name, kind, fetch_dir, write_dir, copy_fetch_dir, copy_write_
         return float(np.mean(v)), len(v)
 
     def copy_kib(directory, counter):
-        v = [val for (_, val) in _pmc_per_dispatch(directory, counter).values()]
-        return max(v)
+        return max(val for (_, val) in _pmc_per_dispatch(directory, counter).values())
 
     gib_kib = float(1 << 20)
     f_scale = gib_kib / copy_kib(copy_fetch_dir, "FETCH_SIZE")
@@ -153,13 +193,88 @@ def record_traffic(name, kind, fetch_dir, write_dir, copy_fetch_dir, copy_write_
     if os.path.exists(path):
         with open(path) as fh:
             data = json.load(fh)
-    data[name] = {"kernel": kernel, "source_hash": source_hash(kind), "bytes_per_launch": int(fetch_b + write_b),
-                  "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
-                  "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-                  "dispatches": {"fetch": nf, "write": nw}}
+    data[name] = {"kernel": kernel, "source_hash": source_hash(kernel_kind(name)),
+                  "bytes_per_launch": int(fetch_b + write_b), "fetch_bytes_per_launch": int(fetch_b),
+                  "write_bytes_per_launch": int(write_b), "fetch_scale": round(f_scale, 4),
+                  "write_scale": round(w_scale, 4), "dispatches": {"fetch": nf, "write": nw}}
     with open(path, "w") as fh:
         json.dump(data, fh, indent=1, sort_keys=True)
     print(json.dumps({name: data[name]}))
+
+
+def summarize(stats_dir, out_md, title, command):
+    """Markdown table of a rocprofv3 --kernel-trace --stats output: per kernel, calls and the
+    average / min / max duration in microseconds (from kernel_stats.csv)."""
+    paths = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_stats.csv under {stats_dir}")
+    rows = []
+    with open(paths[0]) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[5])
+    short = lambda n: n if len(n) <= 90 else n[:87] + "..."
+    lines = [f"# {title}", "", "Command (run from /tmp on the GPU box, $REPO = repository root):", "",
+             f"    {command}", "",
+             "Source: rocprofv3 `--kernel-trace --stats` kernel_stats.csv; durations in microseconds.", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for n, c, a, lo, hi, pct in rows:
+        lines.append(f"| `{short(n)}` | {c} | {a:.2f} | {lo:.2f} | {hi:.2f} | {pct:.1f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out_md)
+
+
+# ------------------------------------------------------------------------------------------
+# CPU oracle baseline: a pool of worker processes forked before the GPU is initialised
+# ------------------------------------------------------------------------------------------
+_CPU_JOB = None   # (task function, number of tasks, seconds); read by the forked workers
+
+
+def _cpu_worker(args):
+    wid, n_workers = args
+    from threadpoolctl import threadpool_limits
+    task, n_tasks, seconds = _CPU_JOB
+    done, n = 0.0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        i = wid
+        while time.perf_counter() - t0 < seconds:
+            done += task(i % n_tasks)
+            n += 1
+            i += n_workers
+    return done, n
+
+
+def cpu_pool(task, n_tasks, seconds, workers):
+    """Runs task(i) (returning the units it processed) on `workers` processes for about `seconds`
+    of wall time; returns (units per second over the pool's wall time, tasks done, wall)."""
+    import multiprocessing as mp
+    global _CPU_JOB
+    _CPU_JOB = (task, n_tasks, seconds)
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        res = pool.map(_cpu_worker, [(w, workers) for w in range(workers)])
+    wall = time.perf_counter() - t0
+    _CPU_JOB = None
+    units = sum(r[0] for r in res)
+    return units / wall, sum(r[1] for r in res), wall
+
+
+def cpu_baseline_record(value, unit, n, wall, workers, what):
+    return {"value": value, "unit": unit, "cores": workers, "kind": "oracle",
+            "sample": f"{n} {what} in {wall:.1f} s wall by {workers} worker processes (fp64 NumPy oracle, BLAS on "
+                      f"one thread each)",
+            "cpu_model": cpu_model(), "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+# ------------------------------------------------------------------------------------------
+# GPU timing and the parity gate
+# ------------------------------------------------------------------------------------------
+def tbits(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
 def time_calls(torch, fn, steps, warmup):
@@ -190,14 +305,15 @@ def time_calls(torch, fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
-def cold_time(torch, fn, steps, scratch):
+def cold_time(torch, fn, steps, dev):
     """Median per-call time with a 1 GiB read before each call (L2 and MALL flushed).
 
     The flush reads a buffer written once beforehand: a write-based flush would leave dirty
     lines whose write-back competes with the timed call."""
-    ts = []
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     scratch.fill_(1)
     flat = scratch.view(torch.int64)
+    ts = []
     for _ in range(steps):
         flat.sum()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -206,62 +322,38 @@ def cold_time(torch, fn, steps, scratch):
         e.record()
         torch.cuda.synchronize()
         ts.append(s.elapsed_time(e))
+    del scratch
     return float(np.median(ts))
 
 
-# ------------------------------------------------------------------------------------------
-# CPU oracle baseline (bounded sample)
-# ------------------------------------------------------------------------------------------
-def cpu_baseline_paged(inp, spec, seconds, bytes_per_seq, trees=None):
-    import oracle
-    from threadpoolctl import threadpool_limits
-    f64 = lambda b: bf16_bits_to_f32(b).astype(np.float64)
-    q, kc, vc = f64(inp["q"]), inp["k_cache"], inp["v_cache"]
-    done_bytes, n = 0, 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < seconds:
-            b = n % spec.batch
-            L = int(inp["kv_lens"][b])
-            pages = inp["page_table"][b, :(L + spec.page_size - 1) // spec.page_size]
-            # the oracle reads only this sequence's pages; pass it a compact pool of them
-            sub_k = f64(kc[pages])
-            sub_v = f64(vc[pages])
-            table = np.arange(len(pages), dtype=np.int32)[None, :]
-            rows = slice(b * spec.q_len, (b + 1) * spec.q_len)
-            if trees is None:
-                oracle.decode_paged(q[rows], sub_k, sub_v, table, np.array([L], dtype=np.int32), inp["sinks"],
-                                    spec.q_len, spec.scale, spec.causal, spec.window)
-            else:
-                oracle.decode_paged_tree(q[rows], sub_k, sub_v, table, np.array([L], dtype=np.int32), trees[rows],
-                                         inp["sinks"], spec.q_len, spec.scale, spec.window)
-            done_bytes += bytes_per_seq[b]
-            n += 1
-    dt = time.perf_counter() - t0
-    return done_bytes / dt / 1e9, n, dt
+def parity_gate(name, out, lse, ro, rl):
+    """Compares sampled rows (those the oracle computed, rl not NaN) with the bar; exits 3 on a
+    mismatch, before anything is timed."""
+    sel = ~np.isnan(rl)
+    o, r = out[sel], ro[sel]
+    err = np.abs(o - r)
+    excess = float((err - (ATOL + RTOL * np.abs(r))).max())
+    ok = bool(np.isfinite(o).all()) and excess <= 0
+    lse_err = 0.0
+    if lse is not None:
+        l, rr = lse[sel], rl[sel]
+        inf = np.isinf(rr)
+        ok = ok and np.array_equal(np.isinf(l), inf) and np.array_equal(l[inf], rr[inf])
+        if (~inf).any():
+            lse_err = float(np.abs(l[~inf] - rr[~inf]).max())
+            ok = ok and lse_err <= LSE_TOL
+    rec = {"rows": int(sel.sum()), "max_abs_err": round(float(err.max()), 6), "max_excess": round(excess, 6),
+           "lse_max_err": round(lse_err, 6), "bar": "|err| <= 1e-2 + 1e-2 |ref|, lse <= 1e-3"}
+    if not ok:
+        print(json.dumps({"error": f"{name}: parity gate failed before timing", "parity": rec}), file=sys.stderr)
+        sys.exit(3)
+    return rec
 
 
-def cpu_baseline_varlen(inp, spec, seconds, flops_per_seq, sinks):
-    import oracle
-    from threadpoolctl import threadpool_limits
-    f64 = lambda b: bf16_bits_to_f32(b).astype(np.float64)
-    cu = inp["cu_seqlens"]
-    done, n = 0.0, 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < seconds:
-            b = n % len(flops_per_seq)
-            s0, s1 = int(cu[b]), int(cu[b + 1])
-            sub_cu = np.array([0, s1 - s0], dtype=np.int32)
-            oracle.prefill_varlen(f64(inp["q"][s0:s1]), f64(inp["k"][s0:s1]), f64(inp["v"][s0:s1]), sub_cu, sub_cu,
-                                  sinks, spec.scale, spec.causal, spec.window)
-            done += flops_per_seq[b]
-            n += 1
-    dt = time.perf_counter() - t0
-    return done / dt / 1e12, n, dt
+def out_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
 
 
-# ------------------------------------------------------------------------------------------
 def pairs_visible(L, causal, window):
     L = np.asarray(L, dtype=np.int64)
     if not causal:
@@ -273,362 +365,572 @@ def pairs_visible(L, causal, window):
     return full * (full + 1) // 2 + np.maximum(L - W, 0) * W
 
 
-def bench_paged(args, torch, amd, name):
-    spec = CONFIGS[name]
-    if args.kv_chunk is not None:
+def block_pairs(lq, lk, rows, causal, window):
+    """Visible (query, key) pairs of the given query rows of a sequence whose Lq queries are the
+    last of its Lk keys."""
+    pos = lk - lq + np.asarray(list(rows), dtype=np.int64)
+    vis = np.minimum(pos + 1, lk) if causal else np.full(len(pos), lk)
+    if window > 0:
+        vis = np.minimum(vis, window)
+    return int(vis.sum())
+
+
+def oracle():
+    import oracle as _oracle
+    return _oracle
+
+
+def spread_block(k, n_blk):
+    """The k-th block of a sample that visits a sequence's n_blk blocks in an order spread over the
+    whole sequence (a stride coprime with n_blk), so that any prefix of the sample covers early and
+    late causal blocks alike."""
+    stride = next(st for st in (29, 31, 37, 41, 43, 1) if np.gcd(st, n_blk) == 1)
+    return (k * stride) % n_blk
+
+
+_SEQ_CACHE = {}
+
+
+def seq_f64(key, make):
+    """The fp64 widening of one sequence's K/V, kept for the next call with the same key (a worker
+    of the CPU pool keeps drawing the same sequence); one entry."""
+    if key not in _SEQ_CACHE:
+        _SEQ_CACHE.clear()
+        _SEQ_CACHE[key] = make()
+    return _SEQ_CACHE[key]
+
+
+# ------------------------------------------------------------------------------------------
+# workloads
+# ------------------------------------------------------------------------------------------
+class Paged:
+    """Paged decode / verify / draft-tree verification (split-KV + merge)."""
+
+    def __init__(self, name, args):
         import dataclasses
-        spec = dataclasses.replace(spec, kv_chunk=args.kv_chunk)
-    inp = make_paged(spec)
-    dev = torch.device("cuda:0")
-    q = tbits(torch, inp["q"], dev)
-    kc = tbits(torch, inp["k_cache"], dev)
-    vc = tbits(torch, inp["v_cache"], dev)
-    table = torch.from_numpy(inp["page_table"]).to(dev)
-    lens = torch.from_numpy(inp["kv_lens"]).to(dev)
-    sinks = torch.from_numpy(inp["sinks"]).to(dev)
-    B, ql, hq, hkv = spec.batch, spec.q_len, spec.hq, spec.hkv
-    need = amd.attn_sink_decode_workspace_size(B, ql, inp["max_kv_len"], hq, 64, spec.kv_chunk)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    out = torch.empty_like(q)
-    lse = torch.empty((B * ql, hq), dtype=torch.float32, device=dev)
-    tree = name == "tree_verify"
-    trees = make_tree_masks(spec) if tree else None
-    trees_d = torch.from_numpy(trees).to(dev) if tree else None
-
-    def step():
-        if tree:
-            amd.attn_sink_decode_paged_tree(q, kc, vc, table, lens, trees_d, sinks, ql, inp["max_kv_len"], spec.scale,
-                                            spec.window, spec.kv_chunk, workspace=ws, out=out, lse=lse)
+        self.name = name
+        spec = CONFIGS[name]
+        if args.kv_chunk is not None:
+            spec = dataclasses.replace(spec, kv_chunk=args.kv_chunk)
+        self.spec = spec
+        self.inp = make_paged(spec)
+        self.tree = name == "tree_verify"
+        self.trees = make_tree_masks(spec) if self.tree else None
+        B, ql, hq, hkv = spec.batch, spec.q_len, spec.hq, spec.hkv
+        L = self.inp["kv_lens"].astype(np.int64)
+        self.kv_bytes_seq = L * hkv * 64 * 2 * 2
+        pages_seq = (L + spec.page_size - 1) // spec.page_size
+        q_bytes = B * ql * hq * 64 * 2
+        tree_bytes = B * ql * 4 if self.tree else 0
+        self.algo_bytes = int(self.kv_bytes_seq.sum() + q_bytes * 2 + B * ql * hq * 4 + pages_seq.sum() * 4 + B * 4
+                              + hq * 4 + tree_bytes)
+        self.kernel_bytes = int(self.kv_bytes_seq.sum() + q_bytes + pages_seq.sum() * 4 + tree_bytes)
+        if self.tree:   # visible keys per row: the prefix plus the row's draft bits
+            bits = np.array([bin(int(x) & ((1 << ql) - 1)).count("1") for x in self.trees],
+                            dtype=np.int64).reshape(B, ql)
+            self.flops = int(((L[:, None] - ql + bits) * hq).sum() * 4 * 64)
         else:
-            amd.attn_sink_decode_paged(q, kc, vc, table, lens, sinks, ql, inp["max_kv_len"], spec.scale, spec.causal,
-                                       spec.window, spec.kv_chunk, workspace=ws, out=out, lse=lse)
+            self.flops = int((L * hkv).sum() * (hq // hkv) * ql * 4 * 64)
 
-    L = inp["kv_lens"].astype(np.int64)
-    kv_bytes_seq = L * hkv * 64 * 2 * 2
-    pages_seq = (L + spec.page_size - 1) // spec.page_size
-    q_bytes = B * ql * hq * 64 * 2
-    tree_bytes = B * ql * 4 if tree else 0
-    algo_bytes = int(kv_bytes_seq.sum() + q_bytes * 2 + B * ql * hq * 4 + pages_seq.sum() * 4 + B * 4 + hq * 4
-                     + tree_bytes)
-    kernel_bytes = int(kv_bytes_seq.sum() + q_bytes + pages_seq.sum() * 4 + tree_bytes)   # split-KV kernel, per launch
-    if tree:   # visible keys per row: the prefix plus the row's draft bits
-        bits = np.array([bin(int(x) & ((1 << ql) - 1)).count("1") for x in trees], dtype=np.int64).reshape(B, ql)
-        flops = int(((L[:, None] - ql + bits) * hq).sum() * 4 * 64)
-    else:
-        flops = int((L * hkv).sum() * (hq // hkv) * ql * 4 * 64)
+    def _oracle_seq(self, b):
+        spec, inp = self.spec, self.inp
+        L = int(inp["kv_lens"][b])
+        pages = inp["page_table"][b, :(L + spec.page_size - 1) // spec.page_size]
+        # the sequence's pages as a compact pool of their own
+        sub_k, sub_v = f64(inp["k_cache"][pages]), f64(inp["v_cache"][pages])
+        table = np.arange(len(pages), dtype=np.int32)[None, :]
+        rows = slice(b * spec.q_len, (b + 1) * spec.q_len)
+        q = f64(inp["q"][rows])
+        lens = np.array([L], dtype=np.int32)
+        if self.tree:
+            return rows, oracle().decode_paged_tree(q, sub_k, sub_v, table, lens, self.trees[rows], inp["sinks"],
+                                                    spec.q_len, spec.scale, spec.window)
+        return rows, oracle().decode_paged(q, sub_k, sub_v, table, lens, inp["sinks"], spec.q_len, spec.scale,
+                                           spec.causal, spec.window)
 
-    ms = time_calls(torch, step, args.steps, args.warmup)
-    # the split-KV kernel alone (the split-only entry point: the same kernel, no merge)
-    def split_only():
-        amd.attn_sink_decode_paged_partials(q, kc, vc, table, lens, sinks, ql, inp["max_kv_len"], spec.scale,
-                                            spec.causal, spec.window, spec.kv_chunk, workspace=ws)
-    split_ms = None if tree else time_calls(torch, split_only, args.steps, args.warmup)
-    # merge kernel alone on the same partials
-    lay = amd.decode_workspace_layout(B, ql, inp["max_kv_len"], hq, spec.kv_chunk)
-    n_p = lay["partials"]
-    o_p = ws[lay["off_o"]:lay["off_o"] + 4 * n_p * hq * 64].view(torch.float32).view(n_p, hq, 64)
-    l_p = ws[lay["off_lse"]:lay["off_lse"] + 4 * n_p * hq].view(torch.float32).view(n_p, hq)
-    indptr = ws[:4 * (lay["rows"] + 1)].view(torch.int32)
-    out2 = torch.empty_like(out)
-    merge_ms = time_calls(torch, lambda: amd.attn_sink_merge_partials(o_p, l_p, indptr, out=out2, return_lse=False),
-                          args.steps, args.warmup)
-    if split_ms is None:   # tree mode has no split-only entry point: the call minus its merge
-        split_ms = ms - merge_ms
-    cold_ms = None
-    if not args.no_cold:
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        cold_ms = cold_time(torch, step, max(5, min(args.steps, 20)), scratch)
-        del scratch
+    def cpu_baseline(self, args, workers):
+        def task(b):
+            self._oracle_seq(b)
+            return float(self.kv_bytes_seq[b])
+        v, n, wall = cpu_pool(task, self.spec.batch, args.cpu_seconds, workers)
+        return cpu_baseline_record(round(v / 1e9, 4), "GB/s", n, wall, workers,
+                                   "sequences of this batch (each worker from its own start, cycling)")
 
-    value = algo_bytes / (ms * 1e-3) / 1e9
-    achieved = kernel_bytes / (split_ms * 1e-3) / 1e9
-    res = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{name}: {B} seqs x q_len {ql}{' (8-node random draft trees)' if tree else ''}, "
-                               f"kv {spec.kv_len[0]}..{spec.kv_len[1]} "
-                               f"(sum {int(L.sum())}), {hq}/{hkv} heads, d 64, {spec.page_size}-token pages, "
-                               f"{spec.kv_chunk}-token chunks, sinks N(0,{spec.sink_std}^2)",
-                   "algorithmic_bytes": algo_bytes, "algorithmic_flops": flops},
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"kernel": "decode_split_kernel", "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(name, "decode"), "algorithmic_bytes_per_launch": kernel_bytes,
-                     "kernel_ms": round(split_ms, 5), "merge_ms": round(merge_ms, 5)},
-    }
-    if cold_ms is not None:
-        res["cold_l2_mall_ms_per_step"] = round(cold_ms, 5)
-        res["cold_value"] = round(algo_bytes / (cold_ms * 1e-3) / 1e9, 1)
-    if not args.no_cpu_baseline:
-        v, n, dt = cpu_baseline_paged(inp, spec, args.cpu_seconds, kv_bytes_seq, trees)
-        res["cpu_baseline"] = {"value": round(v, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{n} sequences of this batch (cycled from sequence 0), {dt:.1f} s wall, "
-                                         f"fp64 NumPy, BLAS limited to 1 thread"}
-    return res
+    def config(self):
+        spec, L = self.spec, self.inp["kv_lens"]
+        return {"workload": f"{self.name}: {spec.batch} seqs x q_len {spec.q_len}"
+                            f"{' (8-node random draft trees)' if self.tree else ''}, kv {spec.kv_len[0]}..{spec.kv_len[1]} "
+                            f"(sum {int(L.sum())}), {spec.hq}/{spec.hkv} heads, d 64, {spec.page_size}-token pages, "
+                            f"{spec.kv_chunk}-token chunks, sinks N(0,{spec.sink_std}^2)",
+                "algorithmic_bytes": self.algo_bytes, "algorithmic_flops": self.flops}
 
+    def gpu(self, torch, amd, args, dev):
+        spec, inp = self.spec, self.inp
+        q, kc, vc = tbits(torch, inp["q"], dev), tbits(torch, inp["k_cache"], dev), tbits(torch, inp["v_cache"], dev)
+        table = torch.from_numpy(inp["page_table"]).to(dev)
+        lens = torch.from_numpy(inp["kv_lens"]).to(dev)
+        sinks = torch.from_numpy(inp["sinks"]).to(dev)
+        B, ql, hq = spec.batch, spec.q_len, spec.hq
+        mkv = inp["max_kv_len"]
+        need = amd.attn_sink_decode_workspace_size(B, ql, mkv, hq, 64, spec.kv_chunk)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((B * ql, hq), dtype=torch.float32, device=dev)
+        trees_d = torch.from_numpy(self.trees).to(dev) if self.tree else None
 
-def bench_varlen(args, torch, amd, name):
-    if name == "embed":
-        specs = [CONFIGS["embed_nosink"], CONFIGS["embed_sink"]]
-    else:
-        specs = [CONFIGS[name]]
-    spec = specs[-1]
-    inp = make_varlen(spec)
-    dev = torch.device("cuda:0")
-    q, k, v = (tbits(torch, inp[x], dev) for x in ("q", "k", "v"))
-    cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
-    sinks = torch.from_numpy(inp["sinks"]).to(dev)
-    out = torch.empty_like(q)
-    lse = torch.empty((q.shape[0], spec.hq), dtype=torch.float32, device=dev)
-    mx = inp["max_seqlen"]
+        def step():
+            if self.tree:
+                amd.attn_sink_decode_paged_tree(q, kc, vc, table, lens, trees_d, sinks, ql, mkv, spec.scale,
+                                                spec.window, spec.kv_chunk, workspace=ws, out=out, lse=lse)
+            else:
+                amd.attn_sink_decode_paged(q, kc, vc, table, lens, sinks, ql, mkv, spec.scale, spec.causal,
+                                           spec.window, spec.kv_chunk, workspace=ws, out=out, lse=lse)
 
-    def one(s, use_sinks):
-        amd.attn_sink_prefill(q, k, v, sinks if use_sinks else None, cu, cu, mx, mx, s.scale, s.causal, s.window,
-                              out=out, lse=lse)
+        def split_only():
+            if self.tree:
+                amd.attn_sink_decode_paged_tree_partials(q, kc, vc, table, lens, trees_d, sinks, ql, mkv, spec.scale,
+                                                         spec.window, spec.kv_chunk, workspace=ws)
+            else:
+                amd.attn_sink_decode_paged_partials(q, kc, vc, table, lens, sinks, ql, mkv, spec.scale, spec.causal,
+                                                    spec.window, spec.kv_chunk, workspace=ws)
 
-    def step():
-        for s in specs:
-            one(s, s.sink_std is not None)
+        # accuracy gate: the timed call on sampled sequences against the oracle
+        step()
+        torch.cuda.synchronize()
+        got_o, got_l = out_np(out), lse.cpu().numpy().astype(np.float64)
+        ro = np.full(got_o.shape, np.nan)
+        rl = np.full(got_l.shape, np.nan)
+        for b in sorted({0, B // 3, (2 * B) // 3, B - 1}):
+            rows, (o, l) = self._oracle_seq(b)
+            ro[rows], rl[rows] = o, l
+        parity = parity_gate(self.name, got_o, got_l, ro, rl)
 
-    lens = inp["seqlens"].astype(np.int64)
-    pairs = pairs_visible(lens, spec.causal, spec.window)
-    flops_seq = pairs * 4 * 64 * spec.hq
-    flops = int(flops_seq.sum()) * len(specs)
-    T = int(lens.sum())
-    io_bytes = T * (spec.hq * 64 * 2 * 2 + spec.hkv * 64 * 2 * 2 + spec.hq * 4)
-    algo_bytes = io_bytes * len(specs)
+        ms = time_calls(torch, step, args.steps, args.warmup)
+        split_ms = time_calls(torch, split_only, args.steps, args.warmup)
+        lay = amd.decode_workspace_layout(B, ql, mkv, hq, spec.kv_chunk)
+        n_p = lay["partials"]
+        o_p = ws[lay["off_o"]:lay["off_o"] + 4 * n_p * hq * 64].view(torch.float32).view(n_p, hq, 64)
+        l_p = ws[lay["off_lse"]:lay["off_lse"] + 4 * n_p * hq].view(torch.float32).view(n_p, hq)
+        indptr = ws[lay["off_indptr"]:lay["off_indptr"] + 4 * (lay["rows"] + 1)].view(torch.int32)
+        out2 = torch.empty_like(out)
+        merge_ms = time_calls(torch, lambda: amd.attn_sink_merge_partials(o_p, l_p, indptr, out=out2, return_lse=False),
+                              args.steps, args.warmup)
+        res = {"value": round(self.algo_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_per_step": round(ms, 5)}
+        res["pct_hbm_peak"] = round(100 * res["value"] / HBM_PEAK_GBS, 2)
+        if not args.no_cold:
+            cold_ms = cold_time(torch, step, max(20, args.steps), dev)
+            res["cold_ms_per_step"] = round(cold_ms, 5)
+            res["cold_value"] = round(self.algo_bytes / (cold_ms * 1e-3) / 1e9, 1)
+            res["cold_pct_hbm_peak"] = round(100 * res["cold_value"] / HBM_PEAK_GBS, 2)
+        achieved = self.kernel_bytes / (split_ms * 1e-3) / 1e9
+        res["roofline"] = {"kernel": "decode_split_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic(self.name, "decode"),
+                           "algorithmic_bytes_per_launch": self.kernel_bytes, "kernel_ms": round(split_ms, 5),
+                           "merge_ms": round(merge_ms, 5)}
+        res["parity_checked"] = True
+        res["parity"] = parity
+        if self.tree:
+            res["tree_overhead"] = self._tree_overhead(torch, amd, args, q, kc, vc, table, lens, sinks, ws, ms,
+                                                       split_ms)
+        return res
 
-    ms = time_calls(torch, step, args.steps, args.warmup)
-    kernel_ms = ms / len(specs)
-    tflops = flops / (ms * 1e-3) / 1e12
-    gbs = algo_bytes / (ms * 1e-3) / 1e9
-    ai = flops / algo_bytes
-    bound = "mfma" if ai > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm"
-    if bound == "mfma":
-        roof = {"kernel": prefill_kernel_name(spec, mx), "bound": "mfma", "achieved": round(flops / len(specs) / (kernel_ms * 1e-3) / 1e12, 2),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"kernel": prefill_kernel_name(spec, mx), "bound": "hbm", "achieved": round(io_bytes / (kernel_ms * 1e-3) / 1e9, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(name, "prefill")
-    roof["algorithmic_flops_per_launch"] = int(flops_seq.sum())
-    roof["algorithmic_bytes_per_launch"] = io_bytes
-    roof["kernel_ms"] = round(kernel_ms, 5)
-    res = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{name}: {spec.batch} seqs, lengths {spec.seqlen[0]}..{spec.seqlen[1]} (sum {T}), "
-                               f"{spec.hq}/{spec.hkv} heads, d 64, causal={spec.causal}, window={spec.window}, "
-                               f"passes={len(specs)}",
-                   "algorithmic_flops": flops, "algorithmic_bytes": algo_bytes},
-        "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2), "gb_per_s": round(gbs, 1),
-        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        s = inp["sinks"] if spec.sink_std is not None else np.full(spec.hq, -np.inf, dtype=np.float32)
-        v, n, dt = cpu_baseline_varlen(inp, spec, args.cpu_seconds, flops_seq, s)
-        res["cpu_baseline"] = {"value": round(v, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{n} sequences of this batch (cycled from sequence 0), {dt:.1f} s wall, "
-                                         f"fp64 NumPy, BLAS limited to 1 thread"}
-    return res
+    def _tree_overhead(self, torch, amd, args, q, kc, vc, table, lens, sinks, ws, tree_ms, tree_split_ms):
+        """The same inputs verified as a causal chain (attn_sink_decode_paged, q_len 8): the cost of
+        the per-row bitmaps against the causal mask at the same shape."""
+        spec, mkv = self.spec, self.inp["max_kv_len"]
+        out = torch.empty_like(q)
+
+        def causal_call():
+            amd.attn_sink_decode_paged(q, kc, vc, table, lens, sinks, spec.q_len, mkv, spec.scale, True, spec.window,
+                                       spec.kv_chunk, workspace=ws, out=out, return_lse=False)
+
+        def causal_split():
+            amd.attn_sink_decode_paged_partials(q, kc, vc, table, lens, sinks, spec.q_len, mkv, spec.scale, True,
+                                                spec.window, spec.kv_chunk, workspace=ws)
+
+        c_ms = time_calls(torch, causal_call, args.steps, args.warmup)
+        c_split = time_calls(torch, causal_split, args.steps, args.warmup)
+        return {"tree_ms": round(tree_ms, 5), "causal_chain_ms": round(c_ms, 5),
+                "overhead_pct": round(100 * (tree_ms / c_ms - 1), 2),
+                "tree_split_ms": round(tree_split_ms, 5), "causal_chain_split_ms": round(c_split, 5),
+                "split_overhead_pct": round(100 * (tree_split_ms / c_split - 1), 2),
+                "what": "the same q/K/V/pages at q_len 8: random 8-node trees vs the causal chain"}
 
 
-def chunk_pairs(q_lens, kv_lens, causal, window):
-    """Visible (query, key) pairs per sequence of a chunked prefill (queries are the newest
-    q_len of kv_len tokens)."""
-    out = []
-    for lq, lk in zip(np.asarray(q_lens, dtype=np.int64), np.asarray(kv_lens, dtype=np.int64)):
-        pos = np.arange(lk - lq, lk)
-        vis = np.minimum(pos + 1, lk) if causal else np.full(lq, lk)
-        if window > 0:
-            vis = np.minimum(vis, window)
-        out.append(int(vis.sum()))
-    return np.asarray(out, dtype=np.int64)
+class Varlen:
+    """Packed varlen self-attention: causal / window prefill, embedding batches, tiny case."""
+
+    def __init__(self, name, args):
+        self.name = name
+        self.specs = [CONFIGS["embed_nosink"], CONFIGS["embed_sink"]] if name == "embed" else [CONFIGS[name]]
+        self.spec = self.specs[-1]
+        self.inp = make_varlen(self.spec)
+        spec, lens = self.spec, self.inp["seqlens"].astype(np.int64)
+        self.flops_seq = pairs_visible(lens, spec.causal, spec.window) * 4 * 64 * spec.hq
+        self.flops_pass = int(self.flops_seq.sum())
+        self.flops = self.flops_pass * len(self.specs)
+        T = int(lens.sum())
+        self.io_bytes = T * (spec.hq * 64 * 2 * 2 + spec.hkv * 64 * 2 * 2 + spec.hq * 4)
+        self.algo_bytes = self.io_bytes * len(self.specs)
+        self.long = spec.seqlen[1] >= 1024      # the CPU sample and the gate work on 64-row blocks
+
+    def _sinks(self, s):
+        return self.inp["sinks"] if s.sink_std is not None else np.full(s.hq, -np.inf, dtype=np.float32)
+
+    def _oracle(self, s, b, rows=None):
+        """oracle.attend on sequence b (the given query rows, else all), NaN-free [Lq or rows]."""
+        inp = self.inp
+        cu = inp["cu_seqlens"]
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        kb, vb = seq_f64(("varlen", b), lambda: (f64(inp["k"][s0:s1]), f64(inp["v"][s0:s1])))
+        rows = np.arange(s1 - s0) if rows is None else np.asarray(rows, dtype=np.int64)
+        return rows, oracle().attend(f64(inp["q"][s0 + rows]), kb, vb, self._sinks(s), s.scale, s.causal, s.window,
+                                     q_pos=rows)
+
+    def cpu_baseline(self, args, workers):
+        spec, lens = self.spec, self.inp["seqlens"]
+        if self.long:
+            n_blk = int(lens.max() + 63) // 64
+
+            def task(i):
+                b, blk = i % spec.batch, spread_block(i // spec.batch, n_blk)
+                lq = int(lens[b])
+                rows = list(range(64 * blk, min(64 * blk + 64, lq)))
+                if not rows:
+                    return 0.0
+                self._oracle(spec, b, rows)
+                return float(block_pairs(lq, lq, rows, spec.causal, spec.window) * 4 * 64 * spec.hq)
+            v, n, wall = cpu_pool(task, spec.batch * n_blk, args.cpu_seconds, workers)
+            what = "blocks of 64 query rows (all heads; sequences and blocks cycled)"
+        else:
+            def task(b):
+                self._oracle(spec, b)
+                return float(self.flops_seq[b])
+            v, n, wall = cpu_pool(task, spec.batch, args.cpu_seconds, workers)
+            what = "whole sequences of this batch (cycled)"
+        return cpu_baseline_record(round(v / 1e12, 6), "TFLOP/s", n, wall, workers, what)
+
+    def config(self):
+        spec, T = self.spec, int(self.inp["seqlens"].sum())
+        return {"workload": f"{self.name}: {spec.batch} seqs, lengths {spec.seqlen[0]}..{spec.seqlen[1]} (sum {T}), "
+                            f"{spec.hq}/{spec.hkv} heads, d 64, causal={spec.causal}, window={spec.window}, "
+                            f"passes={len(self.specs)}",
+                "algorithmic_flops": self.flops, "algorithmic_bytes": self.algo_bytes}
+
+    def gpu(self, torch, amd, args, dev):
+        inp, spec = self.inp, self.spec
+        q, k, v = (tbits(torch, inp[x], dev) for x in ("q", "k", "v"))
+        cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+        sinks = torch.from_numpy(inp["sinks"]).to(dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((q.shape[0], spec.hq), dtype=torch.float32, device=dev)
+        mx = inp["max_seqlen"]
+
+        def one(s):
+            amd.attn_sink_prefill(q, k, v, sinks if s.sink_std is not None else None, cu, cu, mx, mx, s.scale,
+                                  s.causal, s.window, out=out, lse=lse)
+
+        def step():
+            for s in self.specs:
+                one(s)
+
+        # accuracy gate, every pass: sampled rows (a 64-row block of the first and of the last
+        # sequence for long sequences, three whole sequences otherwise)
+        lens, cu_h = inp["seqlens"], inp["cu_seqlens"]
+        B = spec.batch
+        gate = None
+        for s in self.specs:
+            one(s)
+            torch.cuda.synchronize()
+            got_o, got_l = out_np(out), lse.cpu().numpy().astype(np.float64)
+            ro = np.full(got_o.shape, np.nan)
+            rl = np.full(got_l.shape, np.nan)
+            if self.long:
+                picks = [(0, list(range(0, min(64, int(lens[0]))))),
+                         (B - 1, list(range(max(0, int(lens[B - 1]) - 64), int(lens[B - 1]))))]
+            else:
+                picks = [(b, None) for b in sorted({0, B // 2, B - 1})]
+            for b, rows in picks:
+                rws, (o, l) = self._oracle(s, b, rows)
+                idx = int(cu_h[b]) + rws
+                ro[idx], rl[idx] = o, l
+            rec = parity_gate(self.name, got_o, got_l, ro, rl)
+            gate = rec if gate is None else {**rec, "rows": gate["rows"] + rec["rows"],
+                                             "max_abs_err": max(gate["max_abs_err"], rec["max_abs_err"]),
+                                             "max_excess": max(gate["max_excess"], rec["max_excess"]),
+                                             "lse_max_err": max(gate["lse_max_err"], rec["lse_max_err"])}
+
+        ms = time_calls(torch, step, args.steps, args.warmup)
+        kernel_ms = ms / len(self.specs)
+        tflops = self.flops / (ms * 1e-3) / 1e12
+        gbs = self.algo_bytes / (ms * 1e-3) / 1e9
+        kname = prefill_kernel_name(spec.window, mx)
+        if self.flops / self.algo_bytes > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+            roof = {"kernel": kname, "bound": "mfma", "achieved": round(self.flops_pass / (kernel_ms * 1e-3) / 1e12, 2),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        else:
+            roof = {"kernel": kname, "bound": "hbm", "achieved": round(self.io_bytes / (kernel_ms * 1e-3) / 1e9, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+        roof["traffic"] = measured_traffic(self.name, "prefill")
+        roof["algorithmic_flops_per_launch"] = self.flops_pass
+        roof["algorithmic_bytes_per_launch"] = self.io_bytes
+        roof["kernel_ms"] = round(kernel_ms, 5)
+        res = {"value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+               "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2), "gb_per_s": round(gbs, 1),
+               "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        if not args.no_cold:
+            cold_ms = cold_time(torch, step, max(20, args.steps), dev)
+            res["cold_ms_per_step"] = round(cold_ms, 5)
+            res["cold_value"] = round(self.flops / (cold_ms * 1e-3) / 1e12, 2)
+        res["roofline"] = roof
+        res["parity_checked"] = True
+        res["parity"] = gate
+        return res
 
 
-def cpu_baseline_chunked(inp, spec, seconds, sinks, block=64):
-    """The fp64 oracle on blocks of 64 chunk rows, cycling over sequences."""
-    import oracle
-    from threadpoolctl import threadpool_limits
-    f64 = lambda b: bf16_bits_to_f32(b).astype(np.float64)
-    cu, lens = inp["cu_seqlens_q"], inp["kv_lens"]
-    q, kc, vc = f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"])  # input widening, not timed
-    done, n = 0.0, 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < seconds:
-            b = n % len(lens)
-            q0, lq = int(cu[b]), int(cu[b + 1] - cu[b])
-            rows = np.arange(min(block, lq))
-            # one sequence at a time, as the varlen baseline does
-            oracle.prefill_paged(q[q0:q0 + lq], kc, vc, inp["page_table"][b:b + 1], np.array([0, lq]), lens[b:b + 1],
-                                 sinks, spec.scale, spec.causal, spec.window, rows={0: rows})
-            pos = int(lens[b]) - lq + rows
-            vis = np.minimum(pos + 1, int(lens[b])) if spec.causal else np.full(len(rows), int(lens[b]))
-            if spec.window > 0:
-                vis = np.minimum(vis, spec.window)
-            done += float(vis.sum()) * 4 * 64 * spec.hq
-            n += 1
-    dt = time.perf_counter() - t0
-    return done / dt / 1e12, n, dt
+class Chunked:
+    """Chunked prefill against the paged cache."""
+
+    def __init__(self, name, args):
+        self.name = name
+        self.spec = spec = CONFIGS[name]
+        self.inp = inp = make_paged_prefill(spec)
+        self.pairs = np.array([block_pairs(int(lq), int(lk), range(int(lq)), spec.causal, spec.window)
+                               for lq, lk in zip(inp["q_lens"], inp["kv_lens"])], dtype=np.int64)
+        self.flops = int((self.pairs * 4 * 64 * spec.hq).sum())
+        T = int(inp["q_lens"].sum())
+        kv_tokens = int(inp["kv_lens"].astype(np.int64).sum())
+        pages = int(((inp["kv_lens"].astype(np.int64) + spec.page_size - 1) // spec.page_size).sum())
+        self.T, self.kv_tokens = T, kv_tokens
+        self.algo_bytes = T * (spec.hq * 64 * 2 * 2 + spec.hq * 4) + kv_tokens * spec.hkv * 64 * 2 * 2 + 4 * pages
+
+    def _oracle(self, b, rows):
+        """oracle.prefill_paged on the given chunk rows of sequence b (its pages as a compact pool)."""
+        spec, inp = self.spec, self.inp
+        cu, lens = inp["cu_seqlens_q"], inp["kv_lens"]
+        q0, lq = int(cu[b]), int(cu[b + 1] - cu[b])
+        L = int(lens[b])
+        pages = inp["page_table"][b, :(L + spec.page_size - 1) // spec.page_size]
+        table = np.arange(len(pages), dtype=np.int32)[None, :]
+        kc, vc = seq_f64(("chunked", b), lambda: (f64(inp["k_cache"][pages]), f64(inp["v_cache"][pages])))
+        rows = np.asarray(rows, dtype=np.int64)
+        # only the rows asked for are widened; the oracle reads no other row of q
+        qb = np.zeros((lq, spec.hq, 64))
+        qb[rows] = f64(inp["q"][q0 + rows])
+        o, l = oracle().prefill_paged(qb, kc, vc, table, np.array([0, lq]), lens[b:b + 1], inp["sinks"], spec.scale,
+                                      spec.causal, spec.window, rows={0: rows})
+        return o[rows], l[rows]
+
+    def cpu_baseline(self, args, workers):
+        spec, inp = self.spec, self.inp
+        n_blk = int(inp["q_lens"].max() + 63) // 64
+
+        def task(i):
+            b, blk = i % spec.batch, spread_block(i // spec.batch, n_blk)
+            lq, lk = int(inp["q_lens"][b]), int(inp["kv_lens"][b])
+            rows = list(range(64 * blk, min(64 * blk + 64, lq)))
+            if not rows:
+                return 0.0
+            self._oracle(b, rows)
+            return float(block_pairs(lq, lk, rows, spec.causal, spec.window) * 4 * 64 * spec.hq)
+        v, n, wall = cpu_pool(task, spec.batch * n_blk, args.cpu_seconds, workers)
+        return cpu_baseline_record(round(v / 1e12, 6), "TFLOP/s", n, wall, workers,
+                                   "blocks of 64 chunk rows (all heads; sequences and blocks cycled)")
+
+    def config(self):
+        spec = self.spec
+        return {"workload": f"{self.name}: {spec.batch} seqs, chunks of {spec.q_len[0]}..{spec.q_len[1]} tokens on "
+                            f"{spec.ctx_len[0]}..{spec.ctx_len[1]} cached (sum {self.T} queries, {self.kv_tokens} "
+                            f"keys), {spec.hq}/{spec.hkv} heads, d 64, {spec.page_size}-token pages, "
+                            f"causal={spec.causal}",
+                "algorithmic_flops": self.flops, "algorithmic_bytes": self.algo_bytes}
+
+    def gpu(self, torch, amd, args, dev):
+        spec, inp = self.spec, self.inp
+        q, kc, vc = (tbits(torch, inp[x], dev) for x in ("q", "k_cache", "v_cache"))
+        table = torch.from_numpy(inp["page_table"]).to(dev)
+        cu = torch.from_numpy(inp["cu_seqlens_q"]).to(dev)
+        lens = torch.from_numpy(inp["kv_lens"]).to(dev)
+        sinks = torch.from_numpy(inp["sinks"]).to(dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((q.shape[0], spec.hq), dtype=torch.float32, device=dev)
+
+        def step():
+            amd.attn_sink_prefill_paged(q, kc, vc, table, cu, lens, sinks, inp["max_q"], inp["max_kv_len"],
+                                        spec.scale, spec.causal, spec.window, out=out, lse=lse)
+
+        step()
+        torch.cuda.synchronize()
+        got_o, got_l = out_np(out), lse.cpu().numpy().astype(np.float64)
+        ro = np.full(got_o.shape, np.nan)
+        rl = np.full(got_l.shape, np.nan)
+        B = spec.batch
+        for b, first in ((0, True), (B - 1, False)):
+            lq = int(inp["q_lens"][b])
+            rows = np.arange(0, min(64, lq)) if first else np.arange(max(0, lq - 64), lq)
+            o, l = self._oracle(b, rows)
+            q0 = int(inp["cu_seqlens_q"][b])
+            ro[q0 + rows], rl[q0 + rows] = o, l
+        parity = parity_gate(self.name, got_o, got_l, ro, rl)
+
+        ms = time_calls(torch, step, args.steps, args.warmup)
+        tflops = self.flops / (ms * 1e-3) / 1e12
+        gbs = self.algo_bytes / (ms * 1e-3) / 1e9
+        kname = prefill_kernel_name(spec.window, inp["max_q"])
+        if self.flops / self.algo_bytes > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+            roof = {"kernel": kname, "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s"}
+        else:
+            roof = {"kernel": kname, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+        roof["traffic"] = measured_traffic(self.name, "prefill")
+        roof["algorithmic_flops_per_launch"] = self.flops
+        roof["algorithmic_bytes_per_launch"] = self.algo_bytes
+        roof["kernel_ms"] = round(ms, 5)
+        res = {"value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+               "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2), "gb_per_s": round(gbs, 1),
+               "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        if not args.no_cold:
+            cold_ms = cold_time(torch, step, max(20, args.steps), dev)
+            res["cold_ms_per_step"] = round(cold_ms, 5)
+            res["cold_value"] = round(self.flops / (cold_ms * 1e-3) / 1e12, 2)
+        res["roofline"] = roof
+        res["parity_checked"] = True
+        res["parity"] = parity
+        return res
 
 
-def bench_chunked(args, torch, amd, name):
-    spec = CONFIGS[name]
-    inp = make_paged_prefill(spec)
-    dev = torch.device("cuda:0")
-    q, kc, vc = (tbits(torch, inp[x], dev) for x in ("q", "k_cache", "v_cache"))
-    table = torch.from_numpy(inp["page_table"]).to(dev)
-    cu = torch.from_numpy(inp["cu_seqlens_q"]).to(dev)
-    lens = torch.from_numpy(inp["kv_lens"]).to(dev)
-    sinks = torch.from_numpy(inp["sinks"]).to(dev)
-    out = torch.empty_like(q)
-    lse = torch.empty((q.shape[0], spec.hq), dtype=torch.float32, device=dev)
+class Rope:
+    """YaRN rotary encoding of the chunked-prefill workload's new tokens and their append into the
+    paged cache."""
 
-    def step():
-        amd.attn_sink_prefill_paged(q, kc, vc, table, cu, lens, sinks, inp["max_q"], inp["max_kv_len"], spec.scale,
-                                    spec.causal, spec.window, out=out, lse=lse)
+    def __init__(self, name, args):
+        self.name = name
+        self.spec = spec = CONFIGS["chunked_prefill"]
+        self.inp = inp = make_paged_prefill(spec)
+        T = int(inp["cu_seqlens_q"][-1])
+        rng = np.random.default_rng(11)
+        self.k_new = bf16_round_bits(rng.standard_normal((T, spec.hkv, 64)).astype(np.float32))
+        self.v_new = bf16_round_bits(rng.standard_normal((T, spec.hkv, 64)).astype(np.float32))
+        q_lens = inp["q_lens"].astype(np.int64)
+        row_bytes = (spec.hq * 64 * 2) * 2 + (spec.hkv * 64 * 2) * 4     # q in + out, k/v in + cache out
+        self.bytes_seq = q_lens * row_bytes + q_lens * 4                 # + one page id per token
+        self.algo_bytes = int(self.bytes_seq.sum() + 4 * (2 * spec.batch + 1))
+        self.T = T
 
-    pairs = chunk_pairs(inp["q_lens"], inp["kv_lens"], spec.causal, spec.window)
-    flops_seq = pairs * 4 * 64 * spec.hq
-    flops = int(flops_seq.sum())
-    T = int(inp["q_lens"].sum())
-    kv_tokens = int(inp["kv_lens"].astype(np.int64).sum())
-    pages = int(((inp["kv_lens"].astype(np.int64) + spec.page_size - 1) // spec.page_size).sum())
-    algo_bytes = T * (spec.hq * 64 * 2 * 2 + spec.hq * 4) + kv_tokens * spec.hkv * 64 * 2 * 2 + 4 * pages
+    def _oracle_seq(self, b):
+        inp, P = self.inp, self.inp["k_cache"].shape[2]
+        cu, lens = inp["cu_seqlens_q"], inp["kv_lens"]
+        L = int(lens[b])
+        pages = inp["page_table"][b, :(L + P - 1) // P]
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        freqs, m = oracle().yarn_frequencies(64, ROPE_ARGS["rope_theta"], ROPE_ARGS["yarn_factor"],
+                                             ROPE_ARGS["yarn_original_len"], ROPE_ARGS["yarn_alpha"],
+                                             ROPE_ARGS["yarn_beta"], ramp="turns")
+        return pages, r0, r1, oracle().rope_append(f64(inp["q"][r0:r1]), f64(self.k_new[r0:r1]),
+                                                   f64(self.v_new[r0:r1]), np.array([0, r1 - r0]), lens[b:b + 1],
+                                                   np.arange(len(pages))[None, :], f64(inp["k_cache"][pages]),
+                                                   f64(inp["v_cache"][pages]), freqs, m)
 
-    ms = time_calls(torch, step, args.steps, args.warmup)
-    tflops = flops / (ms * 1e-3) / 1e12
-    gbs = algo_bytes / (ms * 1e-3) / 1e9
-    bound = "mfma" if flops / algo_bytes > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm"
-    kname = "prefill_pp_kernel" if (spec.window <= 0 and inp["max_q"] >= 2048) else "prefill_kernel"
-    if bound == "mfma":
-        roof = {"kernel": kname, "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"kernel": kname, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(name, "prefill")
-    roof["algorithmic_flops_per_launch"] = flops
-    roof["algorithmic_bytes_per_launch"] = algo_bytes
-    roof["kernel_ms"] = round(ms, 5)
-    res = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{name}: {spec.batch} seqs, chunks of {spec.q_len[0]}..{spec.q_len[1]} tokens on "
-                               f"{spec.ctx_len[0]}..{spec.ctx_len[1]} cached (sum {T} queries, {kv_tokens} keys), "
-                               f"{spec.hq}/{spec.hkv} heads, d 64, {spec.page_size}-token pages, causal={spec.causal}",
-                   "algorithmic_flops": flops, "algorithmic_bytes": algo_bytes},
-        "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2), "gb_per_s": round(gbs, 1),
-        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        v, n, dt = cpu_baseline_chunked(inp, spec, args.cpu_seconds, inp["sinks"])
-        res["cpu_baseline"] = {"value": round(v, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{n} blocks of 64 chunk rows (cycling over the sequences), {dt:.1f} s wall, "
-                                         f"fp64 NumPy, BLAS limited to 1 thread"}
-    return res
+    def cpu_baseline(self, args, workers):
+        def task(b):
+            self._oracle_seq(b)
+            return float(self.bytes_seq[b])
+        v, n, wall = cpu_pool(task, self.spec.batch, args.cpu_seconds, workers)
+        return cpu_baseline_record(round(v / 1e9, 4), "GB/s", n, wall, workers,
+                                   "sequences' chunks (each worker from its own start, cycling)")
+
+    def config(self):
+        spec = self.spec
+        return {"workload": f"{self.name}: YaRN rotary encoding (theta 150000, factor 32, original 4096, ramp over "
+                            f"the turns) of {self.T} new tokens ({spec.batch} chunks of 2048 on 0..6144 cached), "
+                            f"{spec.hq}/{spec.hkv} heads, d 64, K/V appended into 16-token pages",
+                "algorithmic_bytes": self.algo_bytes}
+
+    def gpu(self, torch, amd, args, dev):
+        spec, inp = self.spec, self.inp
+        q, kn, vn = tbits(torch, inp["q"], dev), tbits(torch, self.k_new, dev), tbits(torch, self.v_new, dev)
+        kc, vc = tbits(torch, inp["k_cache"], dev), tbits(torch, inp["v_cache"], dev)
+        cu = torch.from_numpy(inp["cu_seqlens_q"]).to(dev)
+        lens = torch.from_numpy(inp["kv_lens"]).to(dev)
+        table = torch.from_numpy(inp["page_table"]).to(dev)
+        q_out = torch.empty_like(q)
+
+        def step():
+            amd.attn_sink_rope_append(q, kn, vn, cu, lens, table, kc, vc, inp["max_q"], inp["max_kv_len"],
+                                      q_out=q_out, yarn_ramp="turns", **ROPE_ARGS)
+
+        step()
+        torch.cuda.synchronize()
+        # gate: rotated q rows and the appended K/V of two sequences (every call writes the same
+        # values, so the timed calls leave the caches as checked here)
+        P = spec.page_size
+        got_q = out_np(q_out)
+        excess, rows = -np.inf, 0
+        for b in (0, spec.batch - 1):
+            pages, r0, r1, (rq, rk, rv) = self._oracle_seq(b)
+            excess = max(excess, float((np.abs(got_q[r0:r1] - rq) - (ATOL + RTOL * np.abs(rq))).max()))
+            idx = torch.from_numpy(pages.astype(np.int64)).to(dev)
+            kc_b, vc_b = out_np(kc[idx]), out_np(vc[idx])
+            L = int(inp["kv_lens"][b])
+            pos = np.arange(L - (r1 - r0), L)
+            gk, ek = kc_b[pos // P, :, pos % P], rk[pos // P, :, pos % P]
+            excess = max(excess, float((np.abs(gk - ek) - (ATOL + RTOL * np.abs(ek))).max()))
+            v_err = float(np.abs(vc_b[pos // P, :, pos % P] - rv[pos // P, :, pos % P]).max())
+            excess = max(excess, v_err if v_err > 0 else -1.0)     # v is copied: exact
+            rows += r1 - r0
+        parity = {"rows": rows, "max_excess": round(excess, 6),
+                  "bar": "|err| <= 1e-2 + 1e-2 |ref| (q, k); v copied exactly"}
+        if not excess <= 0:
+            print(json.dumps({"error": f"{self.name}: parity gate failed before timing", "parity": parity}),
+                  file=sys.stderr)
+            sys.exit(3)
+
+        ms = time_calls(torch, step, args.steps, args.warmup)
+        gbs = self.algo_bytes / (ms * 1e-3) / 1e9
+        res = {"value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(ms, 5),
+               "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        if not args.no_cold:
+            cold_ms = cold_time(torch, step, max(20, args.steps), dev)
+            res["cold_ms_per_step"] = round(cold_ms, 5)
+            res["cold_value"] = round(self.algo_bytes / (cold_ms * 1e-3) / 1e9, 1)
+        res["roofline"] = {"kernel": "rope_append_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic(self.name, "rope"),
+                           "algorithmic_bytes_per_launch": self.algo_bytes, "kernel_ms": round(ms, 5)}
+        res["parity_checked"] = True
+        res["parity"] = parity
+        return res
 
 
-ROPE_ARGS = dict(rope_theta=150000.0, yarn_factor=32.0, yarn_original_len=4096, yarn_alpha=1.0, yarn_beta=32.0)
-
-
-def cpu_baseline_rope(inp, k_new, v_new, seconds, bytes_per_seq):
-    """The fp64 oracle, one sequence at a time (a compact pool of the sequence's pages)."""
-    import oracle
-    from threadpoolctl import threadpool_limits
-    f64 = lambda b: bf16_bits_to_f32(b).astype(np.float64)
-    q, kn, vn = f64(inp["q"]), f64(k_new), f64(v_new)
-    freqs, m = oracle.yarn_frequencies(64, ROPE_ARGS["rope_theta"], ROPE_ARGS["yarn_factor"],
-                                       ROPE_ARGS["yarn_original_len"], ROPE_ARGS["yarn_alpha"], ROPE_ARGS["yarn_beta"])
-    cu, lens = inp["cu_seqlens_q"], inp["kv_lens"]
-    P = inp["k_cache"].shape[2]
-    done, n = 0, 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < seconds:
-            b = n % len(lens)
-            L = int(lens[b])
-            pages = inp["page_table"][b, :(L + P - 1) // P]
-            r0, r1 = int(cu[b]), int(cu[b + 1])
-            oracle.rope_append(q[r0:r1], kn[r0:r1], vn[r0:r1], np.array([0, r1 - r0]), lens[b:b + 1],
-                               np.arange(len(pages))[None, :], f64(inp["k_cache"][pages]), f64(inp["v_cache"][pages]),
-                               freqs, m)
-            done += bytes_per_seq[b]
-            n += 1
-    dt = time.perf_counter() - t0
-    return done / dt / 1e9, n, dt
-
-
-def bench_rope(args, torch, amd, name):
-    spec = CONFIGS["chunked_prefill"]
-    inp = make_paged_prefill(spec)
-    dev = torch.device("cuda:0")
-    T = int(inp["cu_seqlens_q"][-1])
-    rng = np.random.default_rng(11)
-    from workloads import bf16_round_bits
-    k_new = bf16_round_bits(rng.standard_normal((T, spec.hkv, 64)).astype(np.float32))
-    v_new = bf16_round_bits(rng.standard_normal((T, spec.hkv, 64)).astype(np.float32))
-    q, kn, vn = tbits(torch, inp["q"], dev), tbits(torch, k_new, dev), tbits(torch, v_new, dev)
-    kc, vc = tbits(torch, inp["k_cache"], dev), tbits(torch, inp["v_cache"], dev)
-    cu = torch.from_numpy(inp["cu_seqlens_q"]).to(dev)
-    lens = torch.from_numpy(inp["kv_lens"]).to(dev)
-    table = torch.from_numpy(inp["page_table"]).to(dev)
-    q_out = torch.empty_like(q)
-
-    def step():
-        amd.attn_sink_rope_append(q, kn, vn, cu, lens, table, kc, vc, inp["max_q"], inp["max_kv_len"], q_out=q_out,
-                                  **ROPE_ARGS)
-
-    q_lens = inp["q_lens"].astype(np.int64)
-    row_bytes = (spec.hq * 64 * 2) * 2 + (spec.hkv * 64 * 2) * 4     # q in + out, k/v in + cache out
-    bytes_seq = q_lens * row_bytes + q_lens * 4                      # + one page id per token
-    algo_bytes = int(bytes_seq.sum() + 4 * (2 * spec.batch + 1))
-    ms = time_calls(torch, step, args.steps, args.warmup)
-    gbs = algo_bytes / (ms * 1e-3) / 1e9
-    res = {
-        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{name}: YaRN rotary encoding (theta 150000, factor 32, original 4096) of {T} new "
-                               f"tokens ({spec.batch} chunks of 2048 on 0..6144 cached), {spec.hq}/{spec.hkv} heads, "
-                               f"d 64, K/V appended into 16-token pages",
-                   "algorithmic_bytes": algo_bytes},
-        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"kernel": "rope_append_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, "rope"),
-                     "algorithmic_bytes_per_launch": algo_bytes, "kernel_ms": round(ms, 5)},
-    }
-    if not args.no_cpu_baseline:
-        v, n, dt = cpu_baseline_rope(inp, k_new, v_new, args.cpu_seconds, bytes_seq)
-        res["cpu_baseline"] = {"value": round(v, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{n} sequences' chunks (cycled from sequence 0), {dt:.1f} s wall, fp64 "
-                                         f"NumPy, BLAS limited to 1 thread"}
-    return res
+def make_workload(name, args):
+    if name in ("paged_decode", "verify", "tree_verify"):
+        return Paged(name, args)
+    if name == "chunked_prefill":
+        return Chunked(name, args)
+    if name == "rope_append":
+        return Rope(name, args)
+    return Varlen(name, args)
 
 
 def main():
     args = parse()
     if args.record_traffic:
-        kind = ("decode" if args.workload in ("paged_decode", "verify", "tree_verify") else
-                "rope" if args.workload == "rope_append" else "prefill")
-        record_traffic(args.workload, kind, *args.record_traffic)
+        record_traffic("paged_decode" if args.workload == "default" else args.workload, *args.record_traffic)
+        return
+    if args.summarize:
+        summarize(*args.summarize, args.summary_command)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this build measures the "
               f"one-GPU shard of the path).", file=sys.stderr)
         sys.exit(2)
     import torch
-    if not torch.cuda.is_available():
+    if torch.cuda.device_count() < 1:       # counts devices without initialising the GPU
         print("bench.py needs a GPU (HIP device)", file=sys.stderr)
         sys.exit(1)
-    import gqa_attention_sinks_sink_amd as amd
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(3)
         for _ in range(3):
@@ -636,15 +938,34 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30}))
         return
-    if args.workload in ("paged_decode", "verify", "tree_verify"):
-        res = bench_paged(args, torch, amd, args.workload)
-    elif args.workload == "chunked_prefill":
-        res = bench_chunked(args, torch, amd, args.workload)
-    elif args.workload == "rope_append":
-        res = bench_rope(args, torch, amd, args.workload)
-    else:
-        res = bench_varlen(args, torch, amd, args.workload)
-    print(json.dumps(res), flush=True)
+
+    names = ["paged_decode", "causal_prefill"] if args.workload == "default" else [args.workload]
+    work = [make_workload(n, args) for n in names]
+    # The CPU oracle runs first, in processes forked before the GPU is initialised.
+    cpu = {}
+    if not args.no_cpu_baseline:
+        workers = cpu_workers(args)
+        for w in work:
+            cpu[w.name] = w.cpu_baseline(args, workers)
+
+    import gqa_attention_sinks_sink_amd as amd
+    dev = torch.device("cuda:0")
+    results = []
+    for w in work:
+        r = w.gpu(torch, amd, args, dev)
+        r["config"] = w.config()
+        if w.name in cpu:
+            r["cpu_baseline"] = cpu[w.name]
+        results.append(r)
+
+    head = results[0]
+    line = {"metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": head["config"]}
+    line.update({k: v for k, v in head.items() if k not in line})
+    if len(results) > 1:
+        line["prefill"] = results[1]
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
