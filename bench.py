@@ -81,6 +81,9 @@ def parse():
                     help="write a markdown summary of a rocprofv3 --stats output (kernel_stats.csv) to OUT_MD; "
                          "--summary-command names the command that produced it; runs on the host only")
     ap.add_argument("--summary-command", default="", help="the command recorded in a --summarize summary")
+    ap.add_argument("--pmc-table", nargs=2, metavar=("PMC_DIR", "KERNEL"),
+                    help="print, as one JSON line, the per-dispatch average of every counter in a rocprofv3 --pmc "
+                         "output over the dispatches of KERNEL (a name such as prefill_pp_kernel); host only")
     return ap.parse_args()
 
 
@@ -224,6 +227,27 @@ def summarize(stats_dir, out_md, title, command):
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(out_md)
+
+
+def pmc_table(directory, kernel):
+    """Per-dispatch averages of every counter of a rocprofv3 --pmc output over the dispatches of
+    one kernel (counters summed over the chip per dispatch, as rocprofv3 reports them)."""
+    per = {}     # counter -> {dispatch: value}
+    names = set()
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                k = row["Kernel_Name"]
+                if ("::" + kernel + "<") not in k and ("::" + kernel + "(") not in k:
+                    continue
+                names.add(k)
+                d = per.setdefault(row["Counter_Name"], {})
+                d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch of {kernel} under {directory}")
+    out = {"kernel": sorted(names), "dispatches": max(len(v) for v in per.values())}
+    out.update({c: float(np.mean(list(v.values()))) for c, v in sorted(per.items())})
+    print(json.dumps(out))
 
 
 # ------------------------------------------------------------------------------------------
@@ -922,6 +946,9 @@ def main():
         return
     if args.summarize:
         summarize(*args.summarize, args.summary_command)
+        return
+    if args.pmc_table:
+        pmc_table(*args.pmc_table)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this build measures the "
