@@ -81,6 +81,8 @@ def parse():
                     help="write a markdown summary of a rocprofv3 --stats output (kernel_stats.csv) to OUT_MD; "
                          "--summary-command names the command that produced it; runs on the host only")
     ap.add_argument("--summary-command", default="", help="the command recorded in a --summarize summary")
+    ap.add_argument("--summary-workload", default=None,
+                    help="append this workload's HBM traffic (profiles/traffic.json) to a --summarize summary")
     ap.add_argument("--pmc-table", nargs=2, metavar=("PMC_DIR", "KERNEL"),
                     help="print, as one JSON line, the per-dispatch average of every counter in a rocprofv3 --pmc "
                          "output over the dispatches of KERNEL (a name such as prefill_pp_kernel); host only")
@@ -205,9 +207,10 @@ def record_traffic(name, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     print(json.dumps({name: data[name]}))
 
 
-def summarize(stats_dir, out_md, title, command):
+def summarize(stats_dir, out_md, title, command, workload=None):
     """Markdown table of a rocprofv3 --kernel-trace --stats output: per kernel, calls and the
-    average / min / max duration in microseconds (from kernel_stats.csv)."""
+    average / min / max duration in microseconds (from kernel_stats.csv); with a workload, its HBM
+    traffic record from profiles/traffic.json when that was taken on the current kernel source."""
     paths = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no kernel_stats.csv under {stats_dir}")
@@ -224,6 +227,19 @@ def summarize(stats_dir, out_md, title, command):
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for n, c, a, lo, hi, pct in rows:
         lines.append(f"| `{short(n)}` | {c} | {a:.2f} | {lo:.2f} | {hi:.2f} | {pct:.1f} |")
+    if workload is not None:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+            rec = json.load(fh).get(workload)
+        if rec is not None and rec["source_hash"] == source_hash(kernel_kind(workload)):
+            lines += ["", f"HBM traffic of `{rec['kernel']}` per launch (rocprofv3 `--pmc FETCH_SIZE`, then `--pmc "
+                          f"WRITE_SIZE`, each in its own run of `bench.py --workload {workload} --steps 2 --warmup 1 "
+                          f"--no-cold --no-cpu-baseline`; KiB per dispatch scaled so that a plain 1 GiB copy "
+                          f"(`bench.py --calibrate-copy`) reads and writes 1 GiB: fetch x{rec['fetch_scale']}, write "
+                          f"x{rec['write_scale']}; recorded by `bench.py --record-traffic`, source hash "
+                          f"{rec['source_hash']}):", "",
+                      "| fetched bytes | written bytes | total | dispatches averaged |", "|---|---|---|---|",
+                      f"| {rec['fetch_bytes_per_launch']:,} | {rec['write_bytes_per_launch']:,} | "
+                      f"{rec['bytes_per_launch']:,} | {rec['dispatches']['fetch']} |"]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(out_md)
@@ -945,7 +961,7 @@ def main():
         record_traffic("paged_decode" if args.workload == "default" else args.workload, *args.record_traffic)
         return
     if args.summarize:
-        summarize(*args.summarize, args.summary_command)
+        summarize(*args.summarize, args.summary_command, args.summary_workload)
         return
     if args.pmc_table:
         pmc_table(*args.pmc_table)
