@@ -23,7 +23,7 @@ __all__ = [
     "attn_sink_decode_workspace_size",
     "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version", "decode_workspace_layout",
     "attn_sink_decode_workspace_layout", "attn_sink_decode_paged_noalloc", "attn_sink_decode_noalloc_capacity",
-    "attn_sink_decode_paged_tree_partials", "EXPORTED_SYMBOLS",
+    "attn_sink_decode_paged_tree_partials", "attn_sink_decode_paged_range_partials", "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
@@ -32,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "attn_sink_decode_workspace_size", "attn_sink_decode_workspace_layout", "attn_sink_merge_partials",
     "attn_sink_status_string", "attn_sink_version", "attn_sink_decode_paged_noalloc",
     "attn_sink_decode_noalloc_capacity", "attn_sink_decode_paged_tree_partials",
+    "attn_sink_decode_paged_range_partials",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -69,6 +70,10 @@ lib.attn_sink_decode_noalloc_capacity.argtypes = []
 lib.attn_sink_decode_paged_tree_partials.restype = ctypes.c_int
 lib.attn_sink_decode_paged_tree_partials.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _fp, _i32, _i32, _i32,
                                                      _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]
+lib.attn_sink_decode_paged_range_partials.restype = ctypes.c_int
+lib.attn_sink_decode_paged_range_partials.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _fp, _fp, _i32, _i32,
+                                                      _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp,
+                                                      _sz, _vp]
 lib.attn_sink_decode_workspace_size.restype = _sz
 lib.attn_sink_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 lib.attn_sink_decode_workspace_layout.restype = ctypes.c_int
@@ -489,6 +494,34 @@ def attn_sink_decode_paged_tree_partials(q: torch.Tensor, k_cache: torch.Tensor,
                                                   float(softmax_scale), int(window), int(kv_chunk), _ptr(workspace),
                                                   workspace.numel() * workspace.element_size(), _stream(stream))
     _raise(st, "attn_sink_decode_paged_tree_partials")
+    return _partial_views(workspace, batch, q_len, int(max_kv_len), hq, d, kv_chunk)
+
+
+def attn_sink_decode_paged_range_partials(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                          page_table: torch.Tensor, kv_lens: torch.Tensor, kv_start: torch.Tensor,
+                                          kv_total: torch.Tensor, sinks: Optional[torch.Tensor], q_len: int,
+                                          max_kv_len: int, softmax_scale: Optional[float] = None,
+                                          causal: bool = True, window: int = 0, kv_chunk: int = 512,
+                                          workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """The split-KV pass over one key range per sequence (kv_lens[b] keys at absolute positions
+    kv_start[b].. of a kv_total[b]-key sequence); returns the same views as
+    attn_sink_decode_paged_partials."""
+    batch, rows, hq, d, workspace = _decode_args(q, k_cache, v_cache, page_table, kv_lens, sinks, q_len, workspace,
+                                                 kv_chunk, max_kv_len)
+    for t, n in ((kv_start, "kv_start"), (kv_total, "kv_total")):
+        _check(t, n, torch.int32, q.device)
+        if t.numel() != batch:
+            raise ValueError(f"{n} must have batch = {batch} entries")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    num_pages, hkv, page_size = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    st = lib.attn_sink_decode_paged_range_partials(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                                   page_table.shape[1], num_pages, _ptr(kv_lens), _ptr(kv_start),
+                                                   _ptr(kv_total), _ptr(sinks), batch, q_len, int(max_kv_len), hq,
+                                                   hkv, d, page_size, float(softmax_scale), int(bool(causal)),
+                                                   int(window), int(kv_chunk), _ptr(workspace),
+                                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise(st, "attn_sink_decode_paged_range_partials")
     return _partial_views(workspace, batch, q_len, int(max_kv_len), hq, d, kv_chunk)
 
 

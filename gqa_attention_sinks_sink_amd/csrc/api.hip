@@ -491,6 +491,28 @@ attn_sink_status attn_sink_decode_paged_partials(const void* q, const void* k_ca
   return hip_status(launch_decode_split(p, (int)lay.chunks, reinterpret_cast<hipStream_t>(stream)));
 }
 
+attn_sink_status attn_sink_decode_paged_range_partials(const void* q, const void* k_cache, const void* v_cache,
+                                                       const int32_t* page_table, int32_t max_pages_per_seq,
+                                                       int32_t num_pages, const int32_t* kv_lens,
+                                                       const int32_t* kv_start, const int32_t* kv_total,
+                                                       const float* sinks, int32_t batch, int32_t q_len,
+                                                       int32_t max_kv_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                                       int32_t head_dim, int32_t page_size, float softmax_scale,
+                                                       int32_t causal, int32_t window, int32_t kv_chunk,
+                                                       void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeParams p{};
+  DecodeLayout lay;
+  const attn_sink_status st = decode_prepare(q, k_cache, v_cache, page_table, max_pages_per_seq, num_pages, kv_lens,
+                                             sinks, batch, q_len, max_kv_len, num_q_heads, num_kv_heads, head_dim,
+                                             page_size, softmax_scale, causal, window, kv_chunk, workspace,
+                                             workspace_bytes, true, nullptr, false, &p, &lay);
+  if (st != ATTN_SINK_OK || batch == 0) return st;
+  if (kv_start == nullptr || kv_total == nullptr) return ATTN_SINK_ERR_INVALID_ARG;
+  p.kv_start = kv_start;
+  p.kv_total = kv_total;
+  return hip_status(launch_decode_split(p, (int)lay.chunks, reinterpret_cast<hipStream_t>(stream)));
+}
+
 attn_sink_status attn_sink_decode_paged_tree_partials(const void* q, const void* k_cache, const void* v_cache,
                                                       const int32_t* page_table, int32_t max_pages_per_seq,
                                                       int32_t num_pages, const int32_t* kv_lens,

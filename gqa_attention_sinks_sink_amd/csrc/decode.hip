@@ -302,6 +302,15 @@ void decode_split_kernel(DecodeParams p) {
     pid_next = load_page_ids(nxt, 0);
 
     const int b = cur.b, c = cur.c, kvh = cur.kvh, L = cur.L;
+    // Position of the first query token in this range's key numbering, and whether this range
+    // holds key 0 of its sequence (only that range counts the sink).
+    int q0_pos = L - p.q_len;
+    bool seeds_sink = true;
+    if (p.kv_start != nullptr) {
+      const int start = load_invariant(p.kv_start, (size_t)b);
+      q0_pos = load_invariant(p.kv_total, (size_t)b) - p.q_len - start;
+      seeds_sink = start == 0;
+    }
     // ---- keys visible to each column inside this chunk: [vis_lo, vis_hi); wave-wide bounds
     // decide whether a group needs masking at all.
     int vis_lo[NT], vis_hi[NT];
@@ -330,7 +339,7 @@ void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int col = nt * 16 + col_lo;
-      const int pos = L - p.q_len + col / G;
+      const int pos = q0_pos + col / G;
       vis_hi[nt] = (p.causal && !TREE) ? min(cur.chunk_hi, pos + 1) : cur.chunk_hi;
       vis_lo[nt] = (p.window > 0) ? max(cur.chunk_lo, pos - p.window + 1) : cur.chunk_lo;
       if (vis_hi[nt] < vis_lo[nt]) vis_hi[nt] = vis_lo[nt];
@@ -342,7 +351,7 @@ void decode_split_kernel(DecodeParams p) {
       // 0 so the column sum counts it once). Other chunks and waves: m = -inf (d = 1 is inert).
       const int h = kvh * G + (col < R ? col % G : 0);
       const float sink2 = sink_of(h);
-      m[nt] = (c == 0 && w == 0) ? sink2 : kNegInf;
+      m[nt] = (c == 0 && w == 0 && seeds_sink) ? sink2 : kNegInf;
       lsum[nt] = (grp == 0) ? 1.0f : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[nt][dt] = f32x4{0, 0, 0, 0};

@@ -24,6 +24,12 @@ struct DecodeParams {
   // Draft-tree verification when non-null: [batch * q_len] bitmaps, bit i of row b * q_len + t
   // = draft token i visible to token t (the prefix is always visible; causal is not used).
   const int32_t* tree_mask;
+  // One range of each sequence's keys (context parallelism) when non-null: sequence b's
+  // kv_lens[b] keys sit at absolute positions kv_start[b] .. of a sequence of kv_total[b] keys
+  // (queries = its last q_len); masks use absolute positions and only the range starting at
+  // key 0 carries the sink. Null: the range is the whole sequence.
+  const int32_t* kv_start;
+  const int32_t* kv_total;
 };
 
 struct MergeParams {

@@ -305,6 +305,39 @@ attn_sink_status attn_sink_decode_paged_partials(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The split-KV pass over one contiguous range of each sequence's keys, for context
+ * parallelism: the keys of a sequence are spread over several devices, each holding one
+ * range, and each device emits the chunk partials of its range ("GPT-OSS on Day 0", section
+ * "Attention sinks": the attention is split along the sequence, the partials are combined by
+ * their log-sum-exp, and the sink counts once).
+ *
+ *   kv_lens[b]     keys of this range (paged as for attn_sink_decode_paged: page_table row b
+ *                  lists this range's pages, its key 0 first).
+ *   kv_start[b]    int32 [batch] on the device: absolute position of this range's first key.
+ *   kv_total[b]    int32 [batch] on the device: keys of the whole sequence; its last q_len
+ *                  positions are the query tokens.
+ * Causal and window masks use absolute positions: key j of the range is position
+ * kv_start[b] + j, query token t is position kv_total[b] - q_len + t. Only a range with
+ * kv_start[b] == 0 counts the head's sink, so exactly one range of each sequence must start
+ * at 0 (an empty range elsewhere takes any other start). The partials of all ranges of a sequence, listed
+ * per row in any order and merged by attn_sink_merge_partials, give what
+ * attn_sink_decode_paged gives for the whole sequence (up to rounding). A range with no keys
+ * yields one partial: the sink alone if kv_start[b] == 0, else an empty one (lse -inf).
+ * Positions that break 0 <= kv_start[b] <= kv_total[b] - kv_lens[b] give unspecified values
+ * but no out-of-range access (they only enter the masks). kv_start or kv_total NULL (with
+ * batch > 0) is ATTN_SINK_ERR_INVALID_ARG. Everything else, including the workspace layout,
+ * as for attn_sink_decode_paged_partials. Enqueues one kernel.
+ */
+attn_sink_status attn_sink_decode_paged_range_partials(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    const int32_t* kv_lens, const int32_t* kv_start, const int32_t* kv_total, const float* sinks,
+    int32_t batch, int32_t q_len, int32_t max_kv_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    float softmax_scale, int32_t causal, int32_t window, int32_t kv_chunk,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The split-KV pass of attn_sink_decode_paged_tree alone (the tree counterpart of
  * attn_sink_decode_paged_partials): plan and chunk partials in the workspace, no merge.
  * Arguments, constraints and error codes as for attn_sink_decode_paged_tree, without out and

@@ -371,3 +371,28 @@ def test_decode_tree_partials_argument_errors(amd):
     assert _tree_partials(amd, ws_bytes=16) == WS_SMALL
     assert _tree_partials(amd, scale=float("inf")) == INVALID
     assert _tree_partials(amd, batch=0, tree=None) == OK
+
+
+def _range_partials(amd, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, max_pages=512, num_pages=100, kv_lens=FAKE, start=FAKE,
+             total=FAKE, sinks=None, batch=4, q_len=5, max_kv=8192, hq=64, hkv=8, d=64, page=16, scale=0.125,
+             causal=1, window=0, chunk=512, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return amd.lib.attn_sink_decode_paged_range_partials(a["q"], a["k"], a["v"], a["table"], a["max_pages"],
+                                                         a["num_pages"], a["kv_lens"], a["start"], a["total"],
+                                                         a["sinks"], a["batch"], a["q_len"], a["max_kv"], a["hq"],
+                                                         a["hkv"], a["d"], a["page"], a["scale"], a["causal"],
+                                                         a["window"], a["chunk"], a["ws"], a["ws_bytes"],
+                                                         a["stream"])
+
+
+def test_decode_range_partials_argument_errors(amd):
+    assert _range_partials(amd, start=None) == INVALID
+    assert _range_partials(amd, total=None) == INVALID
+    assert _range_partials(amd, q_len=9) == UNSUPPORTED
+    assert _range_partials(amd, chunk=100) == UNSUPPORTED
+    assert _range_partials(amd, ws=None) == INVALID
+    assert _range_partials(amd, ws=FAKE + 16) == INVALID      # workspace not 256-byte aligned
+    assert _range_partials(amd, ws_bytes=16) == WS_SMALL
+    assert _range_partials(amd, hq=60) == INVALID             # not a multiple of hkv
+    assert _range_partials(amd, batch=0, start=None, total=None) == OK
