@@ -86,14 +86,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 __device__ __forceinline__ int k_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int v_swz(int r) { return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1); }
 
-// 16 bytes HBM -> VGPRs, hidden from the compiler's wait-count tracking (the callers wait
-// with wait_vmcnt_tied before using the registers).
-__device__ __forceinline__ u32x4 load_async16(const void* ptr) {
-  u32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(ptr) : "memory");
-  return v;
-}
-
 // s_waitcnt vmcnt(N) (N < 64) that also orders memory accesses for the compiler.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -222,7 +214,10 @@ void decode_split_kernel(DecodeParams p) {
     const int j = l.chunk_lo + kGroupKeys * g;
     return p.page_table[(size_t)l.b * p.max_pages + (j >> p.page_shift)];
   };
-  // Q^T as the B operand (k = head dim), one 16-column tile per nt.
+  // Q^T as the B operand (k = head dim), one 16-column tile per nt. Plain loads, issued at the
+  // end of the previous item: the compiler's wait for them at this item's first product also
+  // retires the groups requested after them (loads return in order), which have landed during
+  // the combine by then (measured: no slower than keeping the wait on the Q loads alone).
   auto load_q = [&](const Loc& l, u32x4 (&qb)[NT][2]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -230,8 +225,8 @@ void decode_split_kernel(DecodeParams p) {
       const int cc = col < R ? col : 0;
       const int t = cc / G, gh = cc - (cc / G) * G;
       const uint16_t* src = p.q + ((size_t)(l.b * p.q_len + t) * p.hq + l.kvh * G + gh) * kHeadDim + grp * 8;
-      qb[nt][0] = load_async16(src);
-      qb[nt][1] = load_async16(src + 32);
+      qb[nt][0] = *reinterpret_cast<const u32x4*>(src);
+      qb[nt][1] = *reinterpret_cast<const u32x4*>(src + 32);
     }
   };
   // DMA of this wave's group g of item l (page id taken from pid, the vector of the group's
@@ -282,18 +277,6 @@ void decode_split_kernel(DecodeParams p) {
   for (int k = 0; k < n_pref; ++k) issue_group(cur, pid, w + kWaves * k, (ring_ctr + k) % S);
 
   for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
-    // Q of this item was requested before its first groups: wait for it (and the older loads).
-    switch (n_pref) {
-      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-      case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-      case 2: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-      case 3: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    }
-    // tie Q to the wait: no use of it may be scheduled above
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(qb[nt][0]), "+v"(qb[nt][1]));
-
     // The next item is located and its page ids loaded on every iteration (the last one
     // re-reads its own): the compiler's wait analysis does not follow branch conditions, and
     // a conditional load would make it wait again after the next item's loads are issued.
