@@ -452,6 +452,9 @@ class Paged:
         spec = CONFIGS[name]
         if args.kv_chunk is not None:
             spec = dataclasses.replace(spec, kv_chunk=args.kv_chunk)
+        # Verify-shaped calls leave the chunk length open: the library's planner picks it from the
+        # lengths on the GPU machine (paged decode keeps the 512-token chunks its workload names).
+        self.planned = args.kv_chunk is None and name in ("verify", "tree_verify")
         self.spec = spec
         self.inp = make_paged(spec)
         self.tree = name == "tree_verify"
@@ -501,10 +504,16 @@ class Paged:
         return {"workload": f"{self.name}: {spec.batch} seqs x q_len {spec.q_len}"
                             f"{' (8-node random draft trees)' if self.tree else ''}, kv {spec.kv_len[0]}..{spec.kv_len[1]} "
                             f"(sum {int(L.sum())}), {spec.hq}/{spec.hkv} heads, d 64, {spec.page_size}-token pages, "
-                            f"{spec.kv_chunk}-token chunks, sinks N(0,{spec.sink_std}^2)",
+                            f"{spec.kv_chunk}-token chunks{' (planner)' if self.planned else ''}, "
+                            f"sinks N(0,{spec.sink_std}^2)",
                 "algorithmic_bytes": self.algo_bytes, "algorithmic_flops": self.flops}
 
     def gpu(self, torch, amd, args, dev):
+        if self.planned:
+            import dataclasses
+            s0 = self.spec
+            chunk = amd.attn_sink_decode_plan_chunk(self.inp["kv_lens"], s0.q_len, s0.hq, s0.hkv, s0.page_size)
+            self.spec = dataclasses.replace(s0, kv_chunk=chunk)
         spec, inp = self.spec, self.inp
         q, kc, vc = tbits(torch, inp["q"], dev), tbits(torch, inp["k_cache"], dev), tbits(torch, inp["v_cache"], dev)
         table = torch.from_numpy(inp["page_table"]).to(dev)
@@ -573,7 +582,40 @@ class Paged:
         if self.tree:
             res["tree_overhead"] = self._tree_overhead(torch, amd, args, q, kc, vc, table, lens, sinks, ws, ms,
                                                        split_ms)
+        if self.name == "paged_decode" and args.kv_chunk is None:
+            res["planner_chunk"] = self._planner_chunk(torch, amd, args, q, kc, vc, table, lens, sinks)
         return res
+
+    def _planner_chunk(self, torch, amd, args, q, kc, vc, table, lens, sinks):
+        """Context, not the metric (the workload names 512-token chunks): the same batch with the
+        chunk length the library's planner picks for it, output checked against the 512-token call."""
+        spec, inp = self.spec, self.inp
+        B, ql, hq, mkv = spec.batch, spec.q_len, spec.hq, inp["max_kv_len"]
+        chunk = amd.attn_sink_decode_plan_chunk(inp["kv_lens"], ql, hq, spec.hkv, spec.page_size)
+        ws = torch.empty(amd.attn_sink_decode_workspace_size(B, ql, mkv, hq, 64, chunk), dtype=torch.uint8, device=q.device)
+        out, lse = torch.empty_like(q), torch.empty((B * ql, hq), dtype=torch.float32, device=q.device)
+        ref_out, ref_lse = torch.empty_like(q), torch.empty_like(lse)
+
+        def call(c, w, o, l):
+            amd.attn_sink_decode_paged(q, kc, vc, table, lens, sinks, ql, mkv, spec.scale, spec.causal, spec.window, c,
+                                       workspace=w, out=o, lse=l)
+
+        ws512 = torch.empty(amd.attn_sink_decode_workspace_size(B, ql, mkv, hq, 64, spec.kv_chunk), dtype=torch.uint8,
+                            device=q.device)
+        call(spec.kv_chunk, ws512, ref_out, ref_lse)
+        call(chunk, ws, out, lse)
+        torch.cuda.synchronize()
+        d_out = float((out.float() - ref_out.float()).abs().max())
+        d_lse = float((lse - ref_lse).abs().max())
+        if d_out > 2e-2 or d_lse > 2e-3:
+            print(f"{self.name}: planner-chunk call differs from the 512-token call (out {d_out}, lse {d_lse})",
+                  file=sys.stderr)
+            sys.exit(3)
+        t = time_calls(torch, lambda: call(chunk, ws, out, lse), args.steps, args.warmup)
+        v = self.algo_bytes / (t * 1e-3) / 1e9
+        return {"kv_chunk": chunk, "ms_per_step": round(t, 5), "value": round(v, 1),
+                "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2), "max_abs_diff_vs_512": round(d_out, 6),
+                "what": "context only: the same batch at the chunk attn_sink_decode_plan_chunk picks"}
 
     def _tree_overhead(self, torch, amd, args, q, kc, vc, table, lens, sinks, ws, tree_ms, tree_split_ms):
         """The same inputs verified as a causal chain (attn_sink_decode_paged, q_len 8): the cost of

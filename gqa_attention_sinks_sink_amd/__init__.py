@@ -16,7 +16,7 @@ _BINDING_NAMES = (
     "attn_sink_merge_partials", "attn_sink_prefill", "attn_sink_status_string", "attn_sink_version",
     "attn_sink_decode_workspace_layout", "decode_workspace_layout", "attn_sink_decode_paged_noalloc",
     "attn_sink_decode_noalloc_capacity", "attn_sink_decode_paged_tree_partials",
-    "attn_sink_decode_paged_range_partials", "lib",
+    "attn_sink_decode_paged_range_partials", "attn_sink_decode_plan_chunk", "lib",
 )
 __all__ = list(_BINDING_NAMES)
 

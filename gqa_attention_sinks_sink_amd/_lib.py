@@ -23,7 +23,8 @@ __all__ = [
     "attn_sink_decode_workspace_size",
     "attn_sink_merge_partials", "attn_sink_status_string", "attn_sink_version", "decode_workspace_layout",
     "attn_sink_decode_workspace_layout", "attn_sink_decode_paged_noalloc", "attn_sink_decode_noalloc_capacity",
-    "attn_sink_decode_paged_tree_partials", "attn_sink_decode_paged_range_partials", "EXPORTED_SYMBOLS",
+    "attn_sink_decode_paged_tree_partials", "attn_sink_decode_paged_range_partials", "attn_sink_decode_plan_chunk",
+    "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
@@ -32,7 +33,7 @@ EXPORTED_SYMBOLS = (
     "attn_sink_decode_workspace_size", "attn_sink_decode_workspace_layout", "attn_sink_merge_partials",
     "attn_sink_status_string", "attn_sink_version", "attn_sink_decode_paged_noalloc",
     "attn_sink_decode_noalloc_capacity", "attn_sink_decode_paged_tree_partials",
-    "attn_sink_decode_paged_range_partials",
+    "attn_sink_decode_paged_range_partials", "attn_sink_decode_plan_chunk",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -74,6 +75,8 @@ lib.attn_sink_decode_paged_range_partials.restype = ctypes.c_int
 lib.attn_sink_decode_paged_range_partials.argtypes = [_vp, _vp, _vp, _fp, _i32, _i32, _fp, _fp, _fp, _fp, _i32, _i32,
                                                       _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp,
                                                       _sz, _vp]
+lib.attn_sink_decode_plan_chunk.restype = ctypes.c_int
+lib.attn_sink_decode_plan_chunk.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_int32)]
 lib.attn_sink_decode_workspace_size.restype = _sz
 lib.attn_sink_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 lib.attn_sink_decode_workspace_layout.restype = ctypes.c_int
@@ -523,6 +526,24 @@ def attn_sink_decode_paged_range_partials(q: torch.Tensor, k_cache: torch.Tensor
                                                    workspace.numel() * workspace.element_size(), _stream(stream))
     _raise(st, "attn_sink_decode_paged_range_partials")
     return _partial_views(workspace, batch, q_len, int(max_kv_len), hq, d, kv_chunk)
+
+
+def attn_sink_decode_plan_chunk(kv_lens, q_len: int, num_q_heads: int, num_kv_heads: int, page_size: int,
+                                workgroups: int = 0) -> int:
+    """kv_chunk for a decode call with these host-side lengths (any int sequence, numpy array or CPU
+    tensor); workgroups <= 0 asks the current device for the split kernel's resident grid."""
+    import numpy as np
+    if isinstance(kv_lens, torch.Tensor):
+        if kv_lens.is_cuda:
+            raise ValueError("kv_lens must be host data for the planner")
+        kv_lens = kv_lens.numpy()
+    lens = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32).reshape(-1))
+    out = ctypes.c_int32(0)
+    st = lib.attn_sink_decode_plan_chunk(lens.ctypes.data if lens.size else None, int(lens.size), int(q_len),
+                                         int(num_q_heads), int(num_kv_heads), int(page_size), int(workgroups),
+                                         ctypes.byref(out))
+    _raise(st, "attn_sink_decode_plan_chunk")
+    return int(out.value)
 
 
 def attn_sink_merge_partials(o_partial: torch.Tensor, lse_partial: torch.Tensor, partial_indptr: torch.Tensor,

@@ -7,6 +7,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <mutex>
+#include <vector>
 
 #include "../../include/attn_sink.h"
 #include "common.hpp"
@@ -19,6 +20,9 @@ namespace {
 constexpr int32_t kSupportedHeadDim = 64;
 constexpr int32_t kMaxQLen = 8;
 constexpr int32_t kMaxColumns = 64;   // q_len * (num_q_heads / num_kv_heads) per decode workgroup
+// Fixed cost of one split-KV work item (plan, combine, partial, its share of the merge), in
+// keys: fitted to whole-call times of the verify-shaped workloads over chunk lengths 1024-4096.
+constexpr int64_t kPlanItemKeys = 1024;
 constexpr int64_t kMaxGridY = 65535;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -298,6 +302,52 @@ size_t attn_sink_decode_workspace_size(int32_t batch, int32_t q_len, int32_t max
   // The page size only rounds the single-chunk length up; it never changes the chunk count.
   if (!decode_layout(batch, q_len, max_kv_len, num_q_heads, effective_chunk(kv_chunk, max_kv_len, 16), &l)) return 0;
   return l.total;
+}
+
+attn_sink_status attn_sink_decode_plan_chunk(const int32_t* kv_lens, int32_t batch, int32_t q_len,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t page_size,
+                                             int32_t workgroups, int32_t* kv_chunk) {
+  if (kv_chunk == nullptr || batch < 0 || q_len < 1) return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return ATTN_SINK_ERR_INVALID_ARG;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (q_len > kMaxQLen || (int64_t)q_len * group > kMaxColumns) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size < 16 || page_size > 256) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch > 0 && kv_lens == nullptr) return ATTN_SINK_ERR_INVALID_ARG;
+  int64_t grid = workgroups;
+  if (grid <= 0) {
+    grid = decode_resident_workgroups((q_len * group + 15) / 16, false);
+    if (grid <= 0) return ATTN_SINK_ERR_HIP;
+  }
+  int64_t max_len = 0;
+  for (int32_t b = 0; b < batch; ++b) max_len = std::max<int64_t>(max_len, kv_lens[b]);
+  // Candidates: multiples of 256 (and of the page size) up to one chunk per sequence.
+  const int64_t step = std::max<int64_t>(256, page_size);
+  const int64_t top = std::max<int64_t>(step, (max_len + step - 1) / step * step);
+  int64_t best = top, best_load = INT64_MAX;
+  std::vector<int64_t> load((size_t)grid);
+  for (int64_t c = step; c <= top; c += step) {
+    int64_t items = 0;
+    for (int32_t b = 0; b < batch; ++b) items += std::max<int64_t>(1, (std::max(0, kv_lens[b]) + c - 1) / c);
+    items *= num_kv_heads;
+    if (items > 64 * grid && c != top) continue;  // much finer than the grid: never the cheapest
+    std::fill(load.begin(), load.end(), 0);
+    int64_t i = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t L = std::max(0, kv_lens[b]);
+      const int64_t n = std::max<int64_t>(1, (L + c - 1) / c);
+      for (int64_t ch = 0; ch < n; ++ch) {
+        const int64_t keys = std::max<int64_t>(0, std::min(c, L - ch * c));
+        for (int32_t h = 0; h < num_kv_heads; ++h, ++i) load[(size_t)(i % grid)] += keys + kPlanItemKeys;
+      }
+    }
+    const int64_t worst = *std::max_element(load.begin(), load.end());
+    if (worst <= best_load) {  // ties go to the longer chunk (fewer partials to merge)
+      best_load = worst;
+      best = c;
+    }
+  }
+  *kv_chunk = (int32_t)std::min<int64_t>(best, INT32_MAX / 2 / step * step);
+  return ATTN_SINK_OK;
 }
 
 attn_sink_status attn_sink_decode_workspace_layout(int32_t batch, int32_t q_len, int32_t max_kv_len,

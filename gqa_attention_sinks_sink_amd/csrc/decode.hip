@@ -580,6 +580,12 @@ const DeviceShape& device_shape() {
 }
 }  // namespace
 
+int decode_resident_workgroups(int column_tiles, bool tree) {
+  if (column_tiles < 1 || column_tiles > 4) return 0;
+  const DeviceShape& ds = device_shape();
+  return ds.cus * ds.blocks_per_cu[tree ? 1 : 0][column_tiles];
+}
+
 hipError_t launch_decode_split(const DecodeParams& p, int max_chunks, hipStream_t stream) {
   const int R = p.q_len * p.group;
   const int nt = (R + 15) / 16;

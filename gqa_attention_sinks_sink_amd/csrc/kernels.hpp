@@ -82,6 +82,8 @@ struct RopeParams {
 };
 
 hipError_t launch_decode_split(const DecodeParams& p, int max_chunks, hipStream_t stream);
+// Workgroups of the split-KV kernel resident at once on the current device (its persistent grid).
+int decode_resident_workgroups(int column_tiles, bool tree);
 hipError_t launch_rope_append(const RopeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);

@@ -353,6 +353,29 @@ attn_sink_status attn_sink_decode_paged_tree_partials(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chooses kv_chunk for a decode call from the sequences' lengths, which the caller knows on
+ * the host (the plan metadata a serving runtime builds before attention: "Accelerating
+ * Sonar through speculation", inference runtime section). The split-KV kernel deals its
+ * work items (sequence, chunk, KV head) to a fixed grid of resident workgroups round-robin,
+ * and a call lasts as long as its most loaded workgroup. For every candidate length (the
+ * multiples of max(256, page_size) up to one chunk per sequence) this function deals the
+ * items the same way. It charges each item its keys plus a fixed cost of 1024 keys, which
+ * was fitted on MI355X to whole-call times of the verify-shaped workloads. It returns the
+ * candidate whose most loaded workgroup is lightest; ties go to the longer chunk.
+ *   kv_lens      int32 [batch] on the HOST: the lengths the call will see.
+ *   workgroups   resident workgroups of the split kernel; <= 0 asks the current device
+ *                (a HIP device must then be present).
+ *   kv_chunk     out: the chosen length, a positive multiple of 64 and of page_size.
+ * q_len, num_q_heads, num_kv_heads and page_size are constrained as for
+ * attn_sink_decode_paged. Host arithmetic only, nothing enqueued; size the workspace for
+ * the returned chunk. NULL kv_chunk, or NULL kv_lens with batch > 0, is
+ * ATTN_SINK_ERR_INVALID_ARG.
+ */
+attn_sink_status attn_sink_decode_plan_chunk(const int32_t* kv_lens, int32_t batch, int32_t q_len,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t page_size,
+                                             int32_t workgroups, int32_t* kv_chunk);
+
+/*
  * Bytes of workspace attn_sink_decode_paged needs for these host scalars (0 if they are
  * invalid). Monotone non-decreasing in batch, q_len, max_kv_len and num_q_heads.
  */

@@ -396,3 +396,75 @@ def test_decode_range_partials_argument_errors(amd):
     assert _range_partials(amd, ws_bytes=16) == WS_SMALL
     assert _range_partials(amd, hq=60) == INVALID             # not a multiple of hkv
     assert _range_partials(amd, batch=0, start=None, total=None) == OK
+
+
+def _plan(amd, lens, q_len=5, hq=64, hkv=8, page=16, wgs=512):
+    import ctypes
+    import numpy as np
+    out = ctypes.c_int32(-1)
+    arr = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+    st = amd.lib.attn_sink_decode_plan_chunk(arr.ctypes.data if arr.size else None, int(arr.size), q_len, hq, hkv,
+                                             page, wgs, ctypes.byref(out))
+    return st, out.value
+
+
+def _plan_model(lens, hkv, page, wgs, item_keys=1024):
+    """The planner's documented rule, written out: deal (sequence, chunk, KV head) items
+    round-robin to wgs workgroups, charge keys + item_keys each, keep the chunk whose most loaded
+    workgroup is lightest (ties: the longer chunk)."""
+    step = max(256, page)
+    top = max(step, -(-max([0] + list(lens)) // step) * step)
+    best = None
+    for c in range(step, top + 1, step):
+        items = sum(max(1, -(-max(0, L) // c)) for L in lens) * hkv
+        if items > 64 * wgs and c != top:
+            continue
+        load = [0] * wgs
+        i = 0
+        for L in lens:
+            L = max(0, L)
+            for ch in range(max(1, -(-L // c))):
+                keys = max(0, min(c, L - ch * c))
+                for _ in range(hkv):
+                    load[i % wgs] += keys + item_keys
+                    i += 1
+        w = max(load)
+        if best is None or w <= best[0]:
+            best = (w, c)
+    return best[1]
+
+
+def test_plan_chunk_argument_errors(amd):
+    import ctypes
+    out = ctypes.c_int32(0)
+    assert amd.lib.attn_sink_decode_plan_chunk(None, 3, 5, 64, 8, 16, 512, ctypes.byref(out)) == INVALID
+    assert _plan(amd, [100], q_len=9)[0] == UNSUPPORTED
+    assert _plan(amd, [100], page=8)[0] == UNSUPPORTED
+    assert _plan(amd, [100], hq=60)[0] == INVALID
+    assert amd.lib.attn_sink_decode_plan_chunk(None, 0, 5, 64, 8, 16, 512, None) == INVALID
+    assert _plan(amd, []) == (OK, 256)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_chunk_follows_its_rule(amd, seed):
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    batch = int(rng.integers(1, 40))
+    lens = rng.integers(0, 20000, size=batch).tolist()
+    page = int(rng.choice([16, 64, 256]))
+    hkv = int(rng.choice([1, 2, 8]))
+    wgs = int(rng.choice([64, 512, 1024]))
+    st, c = _plan(amd, lens, hq=hkv * 4, hkv=hkv, page=page, wgs=wgs)
+    assert st == OK
+    assert c % 64 == 0 and c % page == 0 and c >= 256
+    assert c == _plan_model(lens, hkv, page, wgs)
+
+
+def test_plan_chunk_on_the_verify_workloads(amd):
+    """On the verify-shaped bench workloads the rule picks the chunk lengths that measured fastest
+    on MI355X among 1024-7424 (verify 5632, 101.5 us vs 116.1 at 2048; draft trees 7168)."""
+    from workloads import CONFIGS, make_paged
+    for name, want in (("verify", 5632), ("tree_verify", 7168)):
+        spec = CONFIGS[name]
+        lens = make_paged(spec)["kv_lens"]
+        assert _plan(amd, lens, q_len=spec.q_len, hq=spec.hq, hkv=spec.hkv, page=spec.page_size) == (OK, want)

@@ -667,3 +667,15 @@ def test_graph_capture_replays_match_eager(amd):
         for a, b in zip((out, lse, pout, plse), ref):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b), f"replay {rep}"
+
+
+def test_decode_with_the_planned_chunk(amd):
+    """The planner's chunk (asked of the device: workgroups = 0) is a valid kv_chunk, and a decode
+    call with it matches the oracle."""
+    spec = scaled(CONFIGS["verify"], batch=6, q_len=5, kv_len=(1, 3000), hq=16, hkv=2, seed=72)
+    inp = make_paged(spec)
+    chunk = amd.attn_sink_decode_plan_chunk(inp["kv_lens"], spec.q_len, spec.hq, spec.hkv, spec.page_size)
+    assert chunk % 64 == 0 and chunk % spec.page_size == 0 and chunk >= 256
+    out, lse = run_decode(amd, dev_paged(inp), inp, spec, chunk=chunk)
+    ro, rl = oracle_decode(inp, spec)
+    assert_close(out, lse, ro, rl, f"planned chunk {chunk}")
