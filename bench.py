@@ -53,7 +53,8 @@ KERNEL_SOURCES = {
     "prefill": ["prefill.hip", "common.hpp", "kernels.hpp"],
 }
 WORKLOADS = ["default", "paged_decode", "verify", "tree_verify", "causal_prefill", "window_prefill", "embed",
-             "chunked_prefill", "rope_append", "tiny_causal"]
+             "chunked_prefill", "rope_append", "tiny_causal", "paged_decode_tp4", "causal_prefill_tp4"]
+DECODE_WORKLOADS = ("paged_decode", "verify", "tree_verify", "paged_decode_tp4")
 ROPE_ARGS = dict(rope_theta=150000.0, yarn_factor=32.0, yarn_original_len=4096, yarn_alpha=1.0, yarn_beta=32.0)
 
 
@@ -155,7 +156,7 @@ def prefill_kernel_name(window, max_seqlen):
 
 
 def dominant_kernel(name):
-    if name in ("paged_decode", "verify", "tree_verify", "default"):
+    if name in DECODE_WORKLOADS + ("default",):
         return "decode_split_kernel"
     if name == "rope_append":
         return "rope_append_kernel"
@@ -167,7 +168,7 @@ def dominant_kernel(name):
 
 
 def kernel_kind(name):
-    return ("decode" if name in ("paged_decode", "verify", "tree_verify", "default") else
+    return ("decode" if name in DECODE_WORKLOADS + ("default",) else
             "rope" if name == "rope_append" else "prefill")
 
 
@@ -582,7 +583,7 @@ class Paged:
         if self.tree:
             res["tree_overhead"] = self._tree_overhead(torch, amd, args, q, kc, vc, table, lens, sinks, ws, ms,
                                                        split_ms)
-        if self.name == "paged_decode" and args.kv_chunk is None:
+        if self.name in ("paged_decode", "paged_decode_tp4") and args.kv_chunk is None:
             res["planner_chunk"] = self._planner_chunk(torch, amd, args, q, kc, vc, table, lens, sinks)
         return res
 
@@ -988,7 +989,7 @@ class Rope:
 
 
 def make_workload(name, args):
-    if name in ("paged_decode", "verify", "tree_verify"):
+    if name in DECODE_WORKLOADS:
         return Paged(name, args)
     if name == "chunked_prefill":
         return Chunked(name, args)

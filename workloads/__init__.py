@@ -162,6 +162,13 @@ CONFIGS = {
                              page_size=16, kv_chunk=2048, sink_std=2.0, seed=6),
     "chunked_prefill": PagedPrefillSpec("chunked_prefill", batch=8, q_len=(2048, 2048), ctx_len=(0, 6144),
                                         hq=64, hkv=8, page_size=16, sink_std=2.0, seed=5),
+    # One GPU's share of the decode and causal prefill workloads under 4-way head sharding
+    # (tensor parallel): each GPU holds 2 of the 8 KV heads and their 16 query heads, with the
+    # same sequences, lengths, pages and chunking.
+    "paged_decode_tp4": PagedSpec("paged_decode_tp4", batch=64, q_len=1, kv_len=(1024, 8192), hq=16, hkv=2,
+                                  page_size=16, kv_chunk=512, sink_std=2.0, seed=1),
+    "causal_prefill_tp4": VarlenSpec("causal_prefill_tp4", batch=8, seqlen=(4096, 4096), hq=16, hkv=2,
+                                     causal=True, window=0, sink_std=2.0, seed=2),
 }
 
 
