@@ -222,7 +222,7 @@ def summarize(stats_dir, out_md, title, command, workload=None):
                          float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     rows.sort(key=lambda x: -x[5])
     short = lambda n: n if len(n) <= 90 else n[:87] + "..."
-    lines = [f"# {title}", "", "Command (run from /tmp on the GPU box, $REPO = repository root):", "",
+    lines = [f"# {title}", "", "Command (run from /tmp on the GPU host, $REPO = repository root):", "",
              f"    {command}", "",
              "Source: rocprofv3 `--kernel-trace --stats` kernel_stats.csv; durations in microseconds.", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
@@ -454,7 +454,8 @@ class Paged:
         if args.kv_chunk is not None:
             spec = dataclasses.replace(spec, kv_chunk=args.kv_chunk)
         # Verify-shaped calls leave the chunk length open: the library's planner picks it from the
-        # lengths on the GPU machine (paged decode keeps the 512-token chunks its workload names).
+        # lengths and the device's workgroup count (paged decode keeps the 512-token chunks its
+        # workload names).
         self.planned = args.kv_chunk is None and name in ("verify", "tree_verify")
         self.spec = spec
         self.inp = make_paged(spec)
@@ -1010,7 +1011,7 @@ def main():
         pmc_table(*args.pmc_table)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this build measures the "
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (it measures the "
               f"one-GPU shard of the path).", file=sys.stderr)
         sys.exit(2)
     import torch
