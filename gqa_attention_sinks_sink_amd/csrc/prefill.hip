@@ -8,12 +8,11 @@
 // addressed through cu_seqlens without padding ("Fast Embeddings on GPUs", section on
 // ragged attention).
 //
-// Work decomposition: one workgroup = 4 waves; a wave owns RB blocks of 32 rows, a row
-// being one (query token, query head) pair. GP query heads of one KV head group are
-// packed into the row dimension so that one K/V tile in LDS serves all of them. Per
-// 64-key tile every K or V fragment read from LDS feeds RB MFMAs (one per row block),
-// which is what keeps LDS traffic below the MFMA time:
-//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS, Q^T held in registers);
+// Work decomposition: a wave owns blocks of 32 rows, a row being one (query token, query
+// head) pair. GP query heads of one KV head group are packed into the row dimension so that
+// one K/V tile in LDS serves all of them. Every K or V fragment read from LDS feeds one MFMA
+// per row block of the wave, which is what keeps LDS traffic below the MFMA time:
+//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K and the wave's Q rows from LDS);
 //   masks computed from indices only on tiles that need them; online softmax in the
 //   exp2 domain with one FMA and one exp per score; O^T += V^T P^T where P^T is the
 //   score tile converted to bf16 and V^T comes out of LDS through ds_read_b64_tr_b16.
@@ -26,8 +25,9 @@
 // has to rule out overflow: terms stay below 2^32, and every term of a row uses the row's
 // current m, so the softmax is unchanged.
 //
-// Two kernels share these steps: a 4-wave kernel (window, short sequences) and an 8-wave
-// "ping-pong" kernel for long sequences (described above prefill_pp_kernel).
+// Two kernels share these steps: a 4-wave kernel for short items (windows, short sequences;
+// 32-key tiles, three or four workgroups per CU) and an 8-wave "ping-pong" kernel for long
+// sequences (64-key tiles, one workgroup per CU; described above prefill_pp_kernel).
 #include <type_traits>
 
 #include "common.hpp"
@@ -38,28 +38,33 @@ namespace attn_sink {
 namespace {
 constexpr int kThreads = 256;
 constexpr int kTileN = 64;          // keys per tile
-constexpr int kStages = 3;          // K/V tiles in flight: the current one and two prefetched
 constexpr int kTileBytes = kTileN * kHeadDim * 2;  // 8 KB of K (or V) per tile
 constexpr int kStageBytes = 2 * kTileBytes;        // K then V
 constexpr float kSumGuard = 4294967296.f;  // fast-path bound (2^32) on a lane's sum of exp2(s - m)
+// The 4-wave kernel streams K/V in 32-key tiles through a ring of two.
+constexpr int kShortTileN = 32;
+constexpr int kShortTileBytes = kShortTileN * kHeadDim * 2;  // 4 KB of K (or V) per tile
+constexpr int kShortStageBytes = 2 * kShortTileBytes;        // K then V
 }  // namespace
 
 template <int GP, int RB, bool PAGED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 2 ? 3 : 4, RB == 2 ? 3 : 4)))
+void prefill_kernel(PrefillParams p) {
   constexpr int ROWS = 128 * RB;  // rows per workgroup
   constexpr int TOK = ROWS / GP;  // query tokens per workgroup
-  // Ring of K/V tiles filled by buffer loads that write LDS directly. A tile row is one key
-  // (128 B = 8 chunks of 16 B); chunk c of row r sits at chunk position c ^ f(r), with
+  constexpr int TN = kShortTileN;
+  // Ring of two 32-key K/V tiles filled by buffer loads that write LDS directly. A tile row is
+  // one key (128 B = 8 chunks of 16 B); chunk c of row r sits at chunk position c ^ f(r), with
   // f = (r >> 1) & 7 for K and ((r >> 1) & 1) * 4 for V. That makes both the 16 B K reads
-  // (16 lanes, 16 rows, one chunk) and the 8 B transposing V reads (32 lanes, 4 rows,
-  // 64 B each) hit 64 distinct banks.
-  __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[kStages][kStageBytes];
-  // Per-wave slice of 32 RB rows x 128 bytes: the wave's Q rows at the start of a pass, its
-  // output rows at the end. With RB = 1 the slices fill the last ring stage, which holds no
-  // tile until the first iteration issues the third one; that keeps the LDS of three
-  // workgroups within one CU.
-  __shared__ __attribute__((aligned(16))) unsigned char out_lds[kThreads / 64][RB == 1 ? 16 : 32 * RB * kHeadDim * 2];
-  static_assert(kStageBytes >= (kThreads / 64) * 32 * kHeadDim * 2, "RB = 1 staging fits one ring stage");
+  // (16 lanes, 16 rows, one chunk) and the 8 B transposing V reads (32 lanes, 4 rows, 64 B
+  // each) hit 64 distinct banks.
+  __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[2][kShortStageBytes];
+  // Per-wave slice of 32 RB rows x 128 bytes: the wave's Q rows during a pass (16-byte chunk c
+  // of row i at chunk position c ^ ((i >> 1) & 7), as for K), its output rows at the end. Q is
+  // read from here for every tile rather than held in registers: with 16 KB of ring and the
+  // slices, three workgroups of 64-row waves (or four of 32-row waves) fit in one CU, and
+  // their waves hide each other's load latency.
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds[kThreads / 64][32 * RB * kHeadDim * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -117,6 +122,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int i = 1; i < GP; ++i) sink_l2 = ((lane & (GP - 1)) == i) ? sv[i] : sink_l2;
     sink_l2 *= kLog2e;
   }
+  unsigned char* const qw = q_lds[w];
 
   // A unit is one row block, or with causal pairing the blocks u and n_blk - 1 - u, whose
   // key ranges add up to about the same length for every unit.
@@ -127,277 +133,197 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int ts = tile * TOK;
   const int te = min(ts + TOK, Lq);
 
-  // This lane's rows: row block rb covers rows w*32*RB + rb*32 + [0, 32). Keys visible to a
-  // row: [vl, vh).
-  auto visible_keys = [&](int rb, int& vl, int& vh) {
-    const int pos = off + ts + ((w * RB + rb) * 32 + r32) / GP;
-    vh = p.causal ? min(Lk, pos + 1) : Lk;
-    vl = (p.window > 0) ? max(0, pos - p.window + 1) : 0;
-    if (vh < vl) vh = vl;
-  };
-  // The wave's slice: row i holds wave row i (row block i / 32); 16-byte chunk c of a row
-  // sits at chunk position c ^ (i & 7).
-  unsigned char* slice;
-  if constexpr (RB == 1) {
-    slice = kv_lds[kStages - 1] + w * (32 * kHeadDim * 2);
-  } else {
-    slice = out_lds[w];
+  // Keys visible to query token t: [vis_lo(t), vis_hi(t)), both non-decreasing in t.
+  auto vis_lo = [&](int t) { return (p.window > 0) ? max(0, off + t - p.window + 1) : 0; };
+  auto vis_hi = [&](int t) { return max(p.causal ? min(Lk, off + t + 1) : Lk, vis_lo(t)); };
+  // This lane's rows: row block rb covers rows w*32*RB + rb*32 + [0, 32), query token
+  // ts + row / GP. The wave's tokens run from t_first to t_last; a tile inside
+  // [lo_max, hi_min) needs no mask, a tile outside [lo_min, hi_max) has no visible key for any
+  // row of the wave and is skipped. (Scalar: the bounds follow from the first and last token.)
+  const int t_first = ts + (w * RB * 32) / GP;
+  const int t_last = min(te - 1, ts + ((w + 1) * RB * 32 - 1) / GP);
+  int hi_min = 0x7fffffff, lo_max = -0x7fffffff, hi_max = -0x7fffffff, lo_min = 0x7fffffff;
+  if (t_first < te) {
+    hi_min = vis_hi(t_first);
+    lo_min = vis_lo(t_first);
+    hi_max = vis_hi(t_last);
+    lo_max = vis_lo(t_last);
   }
-  // Q rows of the pass into the slice by DMA, issued before the first K/V tiles (so they
-  // have landed once tile 0 has) and read into registers at the first tile. Rows past the
-  // end load the last valid row (their results are never stored). Addresses come from a
-  // fresh lane id (the compiler would otherwise keep them in spill slots across the loop).
+
+  // Q rows of the pass into the slice by DMA, issued before the first K/V tile (so they have
+  // landed once it has). Rows past the end load the last valid row (their results are never
+  // stored). Addresses come from a fresh lane id (the compiler would otherwise compute them
+  // before the key loop and keep them in spill slots).
   {
     WAIT_LGKMCNT0();  // this wave's reads of the slice (previous pass's output) are done
     const int ln = opaque_lane_id();
 #pragma unroll
     for (int k = 0; k < 4 * RB; ++k) {
       const int i = 8 * k + (ln >> 3);
-      const int r = (w * RB + (i >> 5)) * 32 + (i & 31);
+      const int r = w * RB * 32 + i;
       const int t = min(ts + r / GP, te - 1);
-      const uint32_t voff =
-          ((uint32_t)t * p.hq + head0 + (r % GP)) * (kHeadDim * 2) + (uint32_t)(((ln & 7) ^ (ln >> 3)) << 4);
-      buffer_load16_lds_async(rq, slice + k * 1024, voff);
+      const uint32_t voff = ((uint32_t)t * p.hq + head0 + (r % GP)) * (kHeadDim * 2) +
+                            (uint32_t)(((ln & 7) ^ ((i >> 1) & 7)) << 4);
+      buffer_load16_lds_async(rq, qw + k * 1024, voff);
     }
   }
-  // Q^T as the B operand: column = row, k = head dim (16 per step).
-  u32x4 qb[RB][4];
   float m[RB], lsum[RB];
   f32x16 o[RB][2];
-  int hi_min = 0x7fffffff, lo_max = -0x7fffffff, hi_max = -0x7fffffff, lo_min = 0x7fffffff;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int r = (w * RB + rb) * 32 + r32;
-    const int t = ts + r / GP;
-    const bool row_ok = t < te;
     // Online softmax state; the sink seeds the running max, d starts at 1 (held by lane half 0).
     m[rb] = sink_l2;
     lsum[rb] = (half == 0) ? 1.0f : 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) { o[rb][0][i] = 0.f; o[rb][1][i] = 0.f; }
-    int vl, vh;
-    visible_keys(rb, vl, vh);
-    if (row_ok) {
-      hi_min = min(hi_min, vh);
-      lo_max = max(lo_max, vl);
-      if (vh > vl) {
-        hi_max = max(hi_max, vh);
-        lo_min = min(lo_min, vl);
-      }
-    }
   }
-  // Wave-wide bounds: a tile inside [lo_max, hi_min) needs no mask; a tile outside
-  // [lo_min, hi_max) has no visible key for any row of the wave and is skipped.
-#pragma unroll
-  for (int o2 = 32; o2 >= 1; o2 >>= 1) {
-    hi_min = min(hi_min, __shfl_xor(hi_min, o2, 64));
-    lo_max = max(lo_max, __shfl_xor(lo_max, o2, 64));
-    hi_max = max(hi_max, __shfl_xor(hi_max, o2, 64));
-    lo_min = min(lo_min, __shfl_xor(lo_min, o2, 64));
-  }
-  // wave-uniform: keep them in scalar registers
-  hi_min = __builtin_amdgcn_readfirstlane(hi_min);
-  lo_max = __builtin_amdgcn_readfirstlane(lo_max);
-  hi_max = __builtin_amdgcn_readfirstlane(hi_max);
-  lo_min = __builtin_amdgcn_readfirstlane(lo_min);
 
-  // Key range of the workgroup.
+  // Key range of the workgroup, in 32-key tiles.
   const int p_lo = off + ts, p_hi = off + te - 1;
   int jb = (p.window > 0) ? max(0, p_lo - p.window + 1) : 0;
-  jb &= ~(kTileN - 1);
+  jb &= ~(TN - 1);
   const int je = p.causal ? min(Lk, p_hi + 1) : Lk;
+  const int nt = (je > jb) ? (je - jb + TN - 1) / TN : 0;
 
   // K/V tiles: buffer loads bounded by the sequence's last key return zeros past it (exact
-  // zeros for keys that are masked anyway). Wave w fills rows [16w, 16w + 16) of a tile's K
-  // and V with two 1 KB loads each; lane i writes chunk position i & 7 of row i >> 3. The
-  // loads are hidden from the compiler (its own tracking would wait for all of them before
-  // any LDS read); the waits below retire them explicitly.
+  // zeros for keys that are masked anyway). Wave w fills rows [8w, 8w + 8) of a tile's K and V
+  // with one 1 KB load each; lane i writes chunk position i & 7 of row i >> 3. The loads are
+  // hidden from the compiler (its own tracking would wait for all of them before any LDS read);
+  // the waits below retire them explicitly.
   auto issue_tile = [&](int jt, int st) {
+    const int ln = opaque_lane_id();
+    const int r = 8 * w + (ln >> 3);  // row inside the tile
+    const int pch = ln & 7;
+    unsigned char* dst = kv_lds[st] + 8 * w * 128;
     if constexpr (PAGED) {
-      // Rows [16w, 16w + 16) of the tile are 16 consecutive keys inside one page (pages hold
-      // a power of two >= 16 keys): one 2 KB block of K and one of V for this KV head. The
-      // buffer range stops at the sequence's last key, so rows past it read as zeros.
-      const int kr = jt + 16 * w;
+      // Rows [8w, 8w + 8) of the tile are 8 consecutive keys inside one page (pages hold a
+      // power of two >= 16 keys); the buffer range stops at the sequence's last key, so rows
+      // past it read as zeros.
+      const int kr = jt + 8 * w;
       const int slot = min(kr >> p.page_shift, p.max_pages - 1);
       const int pid = clampi(load_invariant(p.page_table, (size_t)b * p.max_pages + slot), 0, p.num_pages - 1);
-      const uint32_t valid = (uint32_t)clampi(Lk - kr, 0, 16);
+      const uint32_t valid = (uint32_t)clampi(Lk - kr, 0, 8);
       const size_t blk = (((size_t)pid * p.hkv + kvh) * p.page_size + (kr & (p.page_size - 1))) * kHeadDim;
-      const __amdgpu_buffer_rsrc_t pk_r = make_rsrc_uniform(p.k + blk, valid * (kHeadDim * 2));
-      const __amdgpu_buffer_rsrc_t pv_r = make_rsrc_uniform(p.v + blk, valid * (kHeadDim * 2));
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int rr = 8 * ii + (lane >> 3);  // row inside the block
-        const int r = 16 * w + rr;            // row inside the tile
-        const int pch = lane & 7;
-        unsigned char* dst = kv_lds[st] + (16 * w + 8 * ii) * 128;
-        buffer_load16_lds_async(pk_r, dst, (uint32_t)(rr * 128 + ((pch ^ ((r >> 1) & 7)) << 4)));
-        buffer_load16_lds_async(pv_r, dst + kTileBytes, (uint32_t)(rr * 128 + ((pch ^ (((r >> 1) & 1) * 4)) << 4)));
-      }
+      const uint32_t voff = (uint32_t)((ln >> 3) * 128);
+      buffer_load16_lds_async(make_rsrc_uniform(p.k + blk, valid * (kHeadDim * 2)), dst,
+                              voff + (uint32_t)((pch ^ ((r >> 1) & 7)) << 4));
+      buffer_load16_lds_async(make_rsrc_uniform(p.v + blk, valid * (kHeadDim * 2)), dst + kShortTileBytes,
+                              voff + (uint32_t)((pch ^ (((r >> 1) & 1) * 4)) << 4));
       return;
     }
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int r = 16 * w + 8 * ii + (lane >> 3);
-      const int pch = lane & 7;
-      const uint32_t rowoff = (uint32_t)(jt + r) * row_bytes + (uint32_t)kvh * (kHeadDim * 2);
-      unsigned char* dst = kv_lds[st] + (16 * w + 8 * ii) * 128;
-      buffer_load16_lds_async(rk, dst, rowoff + (uint32_t)((pch ^ ((r >> 1) & 7)) * 16));
-      buffer_load16_lds_async(rv, dst + kTileBytes, rowoff + (uint32_t)((pch ^ (((r >> 1) & 1) * 4)) * 16));
-    }
+    const uint32_t rowoff = (uint32_t)(jt + r) * row_bytes + (uint32_t)kvh * (kHeadDim * 2);
+    buffer_load16_lds_async(rk, dst, rowoff + (uint32_t)((pch ^ ((r >> 1) & 7)) << 4));
+    buffer_load16_lds_async(rv, dst + kShortTileBytes, rowoff + (uint32_t)((pch ^ (((r >> 1) & 1) * 4)) << 4));
   };
 
-  // Up to two tiles in flight before the loop; every iteration issues at most one more.
-  // (The first load is issued even for an empty range: it is retired after the loop.)
-  issue_tile(jb, 0);
-  if (jb + kTileN < je) issue_tile(jb + kTileN, 1);
+  // Per-lane LDS offsets. K and Q: row r32 of a 32-row block, 16-byte chunk (2 ks + half) ^ f(row)
+  // (f depends only on the row inside the block). V: the transposing reads of 16-key step kk start
+  // at row 16 kk + 4 (grp >> 1) + (jl >> 2) and row + 8; their swizzle does not depend on kk.
+  auto k_off = [&](int ks) -> uint32_t { return r32 * 128 + (((2 * ks + half) ^ ((r32 >> 1) & 7)) << 4); };
+  auto v_off = [&](int dt) -> uint32_t {
+    const int grp = lane >> 4, jl = lane & 15;
+    const int krow = 4 * (grp >> 1) + (jl >> 2);
+    const int c0 = dt * 32 + 16 * (grp & 1) + 4 * (jl & 3);
+    return krow * 128 + ((((c0 >> 3) ^ (((krow >> 1) & 1) * 4)) << 4) + ((c0 & 7) << 1));
+  };
 
-  // Q into registers once its loads (issued before the tiles) are done. The reads complete
-  // before this wave reaches the first barrier, after which (RB = 1) the third tile may
-  // overwrite the slices.
-  if (jb + kTileN < je) {
-    WAIT_VMCNT(8);
-  } else {
-    WAIT_VMCNT(4);
-  }
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qb[rb][ks] = *reinterpret_cast<const u32x4*>(slice + (rb * 32 + r32) * 128 + (((2 * ks + half) ^ (r32 & 7)) << 4));
-  WAIT_LGKMCNT0();
-
-  int st = 0;
-  for (int jt = jb; jt < je; jt += kTileN) {
-    // This wave's loads of the current tile are done once at most the 4 loads of the next
-    // tile are outstanding; the barrier makes every wave's part visible and also means
-    // every wave is done with the stage the new loads overwrite.
-    if (jt + kTileN < je) {
-      WAIT_VMCNT(4);
-    } else {
-      WAIT_VMCNT(0);
-    }
+  if (nt > 0) issue_tile(jb, 0);
+  for (int j = 0; j < nt; ++j) {
+    const int jt = jb + j * TN;
+    // This wave's loads of tile j (and of Q, issued earlier) are done; the barrier makes every
+    // wave's part visible and means every wave is done with tile j - 1, whose stage the next
+    // tile's loads overwrite.
+    WAIT_VMCNT(0);
     lds_barrier();
-    if (jt + 2 * kTileN < je) issue_tile(jt + 2 * kTileN, st == 0 ? 2 : st - 1);
-    const unsigned char* kt_lds = kv_lds[st];
-    const unsigned char* vt_lds = kv_lds[st] + kTileBytes;
-    st = (st == kStages - 1) ? 0 : st + 1;
+    if (j + 1 < nt) issue_tile(jt + TN, (j + 1) & 1);
+    const unsigned char* kt_lds = kv_lds[j & 1];
+    const unsigned char* vt_lds = kv_lds[j & 1] + kShortTileBytes;
+    if (!(jt < hi_max && jt + TN > lo_min)) continue;
 
-    if (jt < hi_max && jt + kTileN > lo_min) {
-      // a 32-key half needs the mask unless every row of the wave sees all of it
-      const bool need_mask0 = !(jt >= lo_max && jt + 32 <= hi_min);
-      const bool need_mask1 = !(jt + 32 >= lo_max && jt + kTileN <= hi_min);
-      f32x16 s[RB][2];  // S^T per row block and 32-key half
-      // S^T for one 32-key half: k = 64 in 4 steps; each K fragment serves every row block.
-      auto qk_half = [&](int kt) {
+    // S^T = K Q^T for the 32 keys of the tile: k = 64 in 4 steps; each K fragment serves every
+    // row block.
+    f32x16 s[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(kt_lds + k_off(ks));
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[rb][kt][i] = 0.f;
+      for (int rb = 0; rb < RB; ++rb) {
+        const u32x4 qf = *reinterpret_cast<const u32x4*>(qw + rb * 4096 + k_off(ks));
+        s[rb] = mfma32(as_bf16x8(a), as_bf16x8(qf), ks == 0 ? f32x16{} : s[rb]);
+      }
+    }
+    // Masks from indices, unless every row of the wave sees the whole tile.
+    if (!(jt >= lo_max && jt + TN <= hi_min)) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int row = kt * 32 + r32;
-          const u32x4 a = *reinterpret_cast<const u32x4*>(kt_lds + row * 128 + (((2 * ks + half) ^ ((row >> 1) & 7)) << 4));
+      for (int rb = 0; rb < RB; ++rb) {
+        const int t = ts + ((w * RB + rb) * 32 + r32) / GP;
+        const int vl = vis_lo(t), vh = vis_hi(t);
+        const unsigned span = (unsigned)(vh - vl);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) s[rb][kt] = mfma32(as_bf16x8(a), as_bf16x8(qb[rb][ks]), s[rb][kt]);
+        for (int i = 0; i < 16; ++i) {
+          const int jk = jt + 8 * (i >> 2) + 4 * half + (i & 3);
+          s[rb][i] = ((unsigned)(jk - vl) < span) ? s[rb][i] : kNegInf;
         }
-      };
-      auto mask_half = [&](int kt) {
+      }
+    }
+    // P = exp2(c*s - m), packed to bf16 as the B operands of the two PV steps; the per-lane
+    // sums. The fast attempt uses the current m; if the guard trips for any lane, m moves to
+    // the exact running maximum (from S, which is still intact), O and d are rescaled, and P is
+    // redone; the second attempt always passes for finite scores.
+    u32x4 pk[RB][2];
+    float ps[RB];
+    for (int attempt = 0; attempt < 2; ++attempt) {
+      bool ok = true;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          int vl, vh;
-          visible_keys(rb, vl, vh);
-          const unsigned span = (unsigned)(vh - vl);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = jt + kt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            s[rb][kt][i] = ((unsigned)(j - vl) < span) ? s[rb][kt][i] : kNegInf;
-          }
-        }
-      };
-      // P for one row block and 32-key half: p = exp2(c*s - m), packed to bf16 as the B
-      // operands of the two PV steps of that half; returns the per-lane sum. S stays intact.
-      u32x4 pk[RB][2][2];
-      auto exp_half = [&](int kt, int rb, float nm) -> float {
+      for (int rb = 0; rb < RB; ++rb) {
+        const float nm = (m[rb] == kNegInf && attempt > 0) ? 0.f : -m[rb];
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const float e0 = fast_exp2(__builtin_fmaf(s[rb][kt][i], c, nm));
-          const float e1 = fast_exp2(__builtin_fmaf(s[rb][kt][i + 1], c, nm));
+          const float e0 = fast_exp2(__builtin_fmaf(s[rb][i], c, nm));
+          const float e1 = fast_exp2(__builtin_fmaf(s[rb][i + 1], c, nm));
           a0 += e0;
           a1 += e1;
-          pk[rb][kt][i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
+          pk[rb][i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
         }
-        return a0 + a1;
-      };
-      // P and d for one half. The fast attempt uses the current m; if the guard trips for any
-      // lane, m moves to the exact running maximum (from S, which is still intact), O and d
-      // are rescaled, and P is redone; the second attempt always passes for finite scores.
-      auto softmax_half = [&](int kt) {
-        float ps[RB];
-        for (int attempt = 0; attempt < 2; ++attempt) {
-          bool ok = true;
+        ps[rb] = a0 + a1;
+        ok = ok && (ps[rb] <= kSumGuard);  // false for inf / NaN
+      }
+      if (__builtin_expect(!__any(!ok), 1) || attempt > 0) break;
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            ps[rb] = exp_half(kt, rb, (m[rb] == kNegInf && attempt > 0) ? 0.f : -m[rb]);
-            ok = ok && (ps[rb] <= kSumGuard);  // false for inf / NaN
-          }
-          if (__builtin_expect(!__any(!ok), 1) || attempt > 0) break;
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = kNegInf;
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            float mx = kNegInf;
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
+        mx = fmaxf(mx, shfl_xor(mx, 32)) * c;
+        const float m_new = fmaxf(m[rb], mx);
+        const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m[rb] - m_new);
+        m[rb] = m_new;
+        lsum[rb] *= alpha;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[rb][kt][i]);
-            mx = fmaxf(mx, shfl_xor(mx, 32)) * c;
-            const float m_new = fmaxf(m[rb], mx);
-            const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m[rb] - m_new);
-            m[rb] = m_new;
-            lsum[rb] *= alpha;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) { o[rb][0][i] *= alpha; o[rb][1][i] *= alpha; }
-          }
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) lsum[rb] += ps[rb];
-      };
-      // O^T += V^T P^T for the 16 keys of step kk; each V^T fragment serves every row block.
-      auto pv_step = [&](int kk) {
-        const int kt = kk >> 1;
-        const int grp = lane >> 4;
-        const int jl = lane & 15;
-        const int krow = kk * 16 + 4 * (grp >> 1) + (jl >> 2);
-        u32x4 av[2];
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const int c0 = dt * 32 + 16 * (grp & 1) + 4 * (jl & 3);
-          // krow and krow + 8 have the same ((row >> 1) & 1), hence the same swizzle
-          const int cb = (((c0 >> 3) ^ (((krow >> 1) & 1) * 4)) << 4) + ((c0 & 7) << 1);
-          const s16x4 lo = lds_read_tr16(vt_lds + krow * 128 + cb);
-          const s16x4 hi = lds_read_tr16(vt_lds + (krow + 8) * 128 + cb);
-          av[dt] = join_tr16(lo, hi);
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) o[rb][dt] = mfma32(as_bf16x8(av[dt]), as_bf16x8(pk[rb][kt][kk & 1]), o[rb][dt]);
-      };
-
-      // Software pipeline inside the tile: the exps of one half run in the shadow of the
-      // MFMAs of other work (S of the second half, then PV of the first half).
-      qk_half(0);
-      if (need_mask0) mask_half(0);
-      qk_half(1);
-      softmax_half(0);
-      if (need_mask1) mask_half(1);
-      pv_step(0);
-      pv_step(1);
-      softmax_half(1);
-      pv_step(2);
-      pv_step(3);
+        for (int i = 0; i < 16; ++i) { o[rb][0][i] *= alpha; o[rb][1][i] *= alpha; }
+      }
     }
-
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) lsum[rb] += ps[rb];
+    // O^T += V^T P^T in two 16-key steps; each V^T fragment serves every row block.
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 av[2];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        // rows krow and krow + 8 have the same ((row >> 1) & 1), hence the same swizzle
+        const unsigned char* vp = vt_lds + kk * 2048 + v_off(dt);
+        av[dt] = join_tr16(lds_read_tr16(vp), lds_read_tr16(vp + 1024));
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) o[rb][dt] = mfma32(as_bf16x8(av[dt]), as_bf16x8(pk[rb][kk]), o[rb][dt]);
+    }
   }
-  // Retire the loads past the last tile and let every wave finish with the ring before it
-  // is reused.
+  // No key is visible (nt = 0): Q is not needed, but its DMA must land before the slice is
+  // reused for the output. Every wave is done with the ring before the next pass reuses it.
   WAIT_VMCNT(0);
   __syncthreads();
 
@@ -410,7 +336,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // key loop and keep them in spill slots.)
     const int ln = opaque_lane_id();
     const int hf = ln >> 5;
-    unsigned char* ow = slice;
+    unsigned char* ow = qw;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float lt = lsum[rb] + shfl_xor(lsum[rb], 32);
