@@ -48,7 +48,7 @@ constexpr int kShortStageBytes = 2 * kShortTileBytes;        // K then V
 }  // namespace
 
 template <int GP, int RB, bool PAGED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 2 ? 3 : 4, RB == 2 ? 3 : 4)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 2 ? 3 : 5, RB == 2 ? 3 : 5)))
 void prefill_kernel(PrefillParams p) {
   constexpr int ROWS = 128 * RB;  // rows per workgroup
   constexpr int TOK = ROWS / GP;  // query tokens per workgroup
@@ -62,7 +62,7 @@ void prefill_kernel(PrefillParams p) {
   // Per-wave slice of 32 RB rows x 128 bytes: the wave's Q rows during a pass (16-byte chunk c
   // of row i at chunk position c ^ ((i >> 1) & 7), as for K), its output rows at the end. Q is
   // read from here for every tile rather than held in registers: with 16 KB of ring and the
-  // slices, three workgroups of 64-row waves (or four of 32-row waves) fit in one CU, and
+  // slices, three workgroups of 64-row waves (or five of 32-row waves) fit in one CU, and
   // their waves hide each other's load latency.
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds[kThreads / 64][32 * RB * kHeadDim * 2];
 
@@ -154,16 +154,26 @@ void prefill_kernel(PrefillParams p) {
   // landed once it has). Rows past the end load the last valid row (their results are never
   // stored). Addresses come from a fresh lane id (the compiler would otherwise compute them
   // before the key loop and keep them in spill slots).
+  // Row i = 8 k + x of the slice (x = lane / 8) is wave row w RB 32 + i: query token
+  // t_w + (8 k + x) / GP, head head0 + (8 k + x) % GP. GP divides 32, so for GP <= 8 the token
+  // steps by 8 / GP per k and the head stays; for GP = 16 the token steps every second k and
+  // the head alternates between x and 8 + x.
+  const int t_w = ts + (w * RB * 32) / GP;
+  auto row_token = [](int k) { return GP <= 8 ? k * (8 / GP) : (k >> 1); };
+  auto row_head = [](int k) { return GP <= 8 ? 0 : 8 * (k & 1); };
   {
     WAIT_LGKMCNT0();  // this wave's reads of the slice (previous pass's output) are done
     const int ln = opaque_lane_id();
+    const int x = ln >> 3;
+    const uint32_t S = (uint32_t)p.hq * (kHeadDim * 2);  // bytes per token of Q
+    const uint32_t t_lane = (uint32_t)(t_w + (GP <= 8 ? x / GP : 0)) * S;
+    const uint32_t h_lane = (uint32_t)(head0 + (GP <= 8 ? x % GP : x)) * (kHeadDim * 2);
+    const uint32_t t_cap = (uint32_t)(te - 1) * S;
 #pragma unroll
     for (int k = 0; k < 4 * RB; ++k) {
-      const int i = 8 * k + (ln >> 3);
-      const int r = w * RB * 32 + i;
-      const int t = min(ts + r / GP, te - 1);
-      const uint32_t voff = ((uint32_t)t * p.hq + head0 + (r % GP)) * (kHeadDim * 2) +
-                            (uint32_t)(((ln & 7) ^ ((i >> 1) & 7)) << 4);
+      const int i = 8 * k + x;
+      const uint32_t voff = min(t_lane + (uint32_t)row_token(k) * S, t_cap) + h_lane +
+                            (uint32_t)(row_head(k) * (kHeadDim * 2)) + (uint32_t)(((ln & 7) ^ ((i >> 1) & 7)) << 4);
       buffer_load16_lds_async(rq, qw + k * 1024, voff);
     }
   }
@@ -190,10 +200,17 @@ void prefill_kernel(PrefillParams p) {
   // with one 1 KB load each; lane i writes chunk position i & 7 of row i >> 3. The loads are
   // hidden from the compiler (its own tracking would wait for all of them before any LDS read);
   // the waits below retire them explicitly.
-  auto issue_tile = [&](int jt, int st) {
+  // Per-lane parts of a tile's load offsets, kept for the whole pass: lane i writes chunk
+  // position i & 7 of row 8 w + (i >> 3), which holds global chunk (i & 7) ^ f(row).
+  uint32_t k_lane, v_lane;
+  {
     const int ln = opaque_lane_id();
     const int r = 8 * w + (ln >> 3);  // row inside the tile
-    const int pch = ln & 7;
+    const uint32_t row = PAGED ? (uint32_t)(ln >> 3) * (kHeadDim * 2) : (uint32_t)r * row_bytes + (uint32_t)kvh * (kHeadDim * 2);
+    k_lane = row + (uint32_t)(((ln & 7) ^ ((r >> 1) & 7)) << 4);
+    v_lane = row + (uint32_t)(((ln & 7) ^ (((r >> 1) & 1) * 4)) << 4);
+  }
+  auto issue_tile = [&](int jt, int st) {
     unsigned char* dst = kv_lds[st] + 8 * w * 128;
     if constexpr (PAGED) {
       // Rows [8w, 8w + 8) of the tile are 8 consecutive keys inside one page (pages hold a
@@ -204,16 +221,12 @@ void prefill_kernel(PrefillParams p) {
       const int pid = clampi(load_invariant(p.page_table, (size_t)b * p.max_pages + slot), 0, p.num_pages - 1);
       const uint32_t valid = (uint32_t)clampi(Lk - kr, 0, 8);
       const size_t blk = (((size_t)pid * p.hkv + kvh) * p.page_size + (kr & (p.page_size - 1))) * kHeadDim;
-      const uint32_t voff = (uint32_t)((ln >> 3) * 128);
-      buffer_load16_lds_async(make_rsrc_uniform(p.k + blk, valid * (kHeadDim * 2)), dst,
-                              voff + (uint32_t)((pch ^ ((r >> 1) & 7)) << 4));
-      buffer_load16_lds_async(make_rsrc_uniform(p.v + blk, valid * (kHeadDim * 2)), dst + kShortTileBytes,
-                              voff + (uint32_t)((pch ^ (((r >> 1) & 1) * 4)) << 4));
+      buffer_load16_lds_async(make_rsrc_uniform(p.k + blk, valid * (kHeadDim * 2)), dst, k_lane);
+      buffer_load16_lds_async(make_rsrc_uniform(p.v + blk, valid * (kHeadDim * 2)), dst + kShortTileBytes, v_lane);
       return;
     }
-    const uint32_t rowoff = (uint32_t)(jt + r) * row_bytes + (uint32_t)kvh * (kHeadDim * 2);
-    buffer_load16_lds_async(rk, dst, rowoff + (uint32_t)((pch ^ ((r >> 1) & 7)) << 4));
-    buffer_load16_lds_async(rv, dst + kShortTileBytes, rowoff + (uint32_t)((pch ^ (((r >> 1) & 1) * 4)) << 4));
+    buffer_load16_lds_async(rk, dst, k_lane + (uint32_t)jt * row_bytes);
+    buffer_load16_lds_async(rv, dst + kShortTileBytes, v_lane + (uint32_t)jt * row_bytes);
   };
 
   // Per-lane LDS offsets. K and Q: row r32 of a 32-row block, 16-byte chunk (2 ks + half) ^ f(row)
@@ -361,14 +374,15 @@ void prefill_kernel(PrefillParams p) {
       }
     }
     const int cc = ln & 7;
+    const int x = ln >> 3;
+    const int t_lane = t_w + (GP <= 8 ? x / GP : 0);
+    uint16_t* const ob = p.out + ((size_t)(q0 + t_lane) * p.hq + head0 + (GP <= 8 ? x % GP : x)) * kHeadDim + cc * 8;
 #pragma unroll
     for (int k = 0; k < 4 * RB; ++k) {
-      const int i = 8 * k + (ln >> 3);
+      const int i = 8 * k + x;
       const u32x4 v = *reinterpret_cast<const u32x4*>(ow + i * 128 + ((cc ^ (i & 7)) << 4));
-      const int r = (w * RB + (i >> 5)) * 32 + (i & 31);
-      const int t = ts + r / GP;
-      if (t < te)
-        *reinterpret_cast<u32x4*>(p.out + ((size_t)(q0 + t) * p.hq + head0 + (r % GP)) * kHeadDim + cc * 8) = v;
+      if (t_lane + row_token(k) < te)
+        *reinterpret_cast<u32x4*>(ob + ((size_t)row_token(k) * p.hq + row_head(k)) * kHeadDim) = v;
     }
   }
   }  // pass
