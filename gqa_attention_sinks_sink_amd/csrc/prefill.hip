@@ -546,6 +546,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // The per-lane part of the offsets is rebuilt from the lane id at every issue: kept in
     // registers across the pass, it would be spilled, and each reload would wait for every
     // tile in flight.
+    // Per-lane parts of a tile's load offsets (contiguous layout), kept for the pass: lane i
+    // writes chunk position i & 7 of row 8 w + (i >> 3), which holds global chunk (i & 7) ^ f(row);
+    // (r >> 1) & 7 and ((r >> 1) & 1) * 4 for r = 8 w + r8.
+    uint32_t k_lane = 0, v_lane = 0;
+    if constexpr (!PAGED) {
+      const int ln = opaque_lane_id();
+      const int r8 = ln >> 3;
+      const int pch = ln & 7;
+      const int swz_k = (r8 >> 1) | ((w & 1) << 2);
+      const int swz_v = (r8 & 2) << 1;
+      k_lane = (uint32_t)r8 * row_bytes + (uint32_t)((pch ^ swz_k) << 4);
+      v_lane = (uint32_t)r8 * row_bytes + (uint32_t)((pch ^ swz_v) << 4);
+    }
     auto issue_tile = [&](int t) {
       if constexpr (PAGED) {
         // Rows [8w, 8w + 8) of the tile are 8 consecutive keys inside one page (pages hold a
@@ -567,17 +580,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                 (uint32_t)(r8 * 128 + ((pch ^ swz_v) << 4)));
         return;
       }
-      const int ln = opaque_lane_id();
-      const int r8 = ln >> 3;  // row 8 w + r8 of the tile
-      const int pch = ln & 7;
       const uint32_t row0 = (uint32_t)(jb + t * kTileN + 8 * w) * row_bytes + (uint32_t)kvh * (kHeadDim * 2);
-      const uint32_t rowoff = (uint32_t)r8 * row_bytes + row0;
-      // (r >> 1) & 7 and ((r >> 1) & 1) * 4 for r = 8 w + r8.
-      const int swz_k = (r8 >> 1) | ((w & 1) << 2);
-      const int swz_v = (r8 & 2) << 1;
       unsigned char* dst = kv_lds[t & (kRing - 1)] + 8 * w * 128;
-      buffer_load16_lds_async(rk, dst, rowoff + (uint32_t)((pch ^ swz_k) << 4));
-      buffer_load16_lds_async(rv, dst + kTileBytes, rowoff + (uint32_t)((pch ^ swz_v) << 4));
+      buffer_load16_lds_async(rk, dst, k_lane + row0);
+      buffer_load16_lds_async(rv, dst + kTileBytes, v_lane + row0);
     };
     issue_tile(0);
     if (nt > 1) issue_tile(1);
