@@ -253,6 +253,9 @@ void prefill_kernel(PrefillParams p) {
     const unsigned char* vt_lds = kv_lds[j & 1] + kShortTileBytes;
     if (!(jt < hi_max && jt + TN > lo_min)) continue;
 
+    // Issue priority: the waves of a SIMD (three workgroups' worth) are raised while they issue
+    // MFMAs, so the matrix unit is fed first and the softmax of the others fills the VALU.
+    __builtin_amdgcn_s_setprio(3);
     // S^T = K Q^T for the 32 keys of the tile: k = 64 in 4 steps; each K fragment serves every
     // row block.
     f32x16 s[RB];
@@ -265,6 +268,7 @@ void prefill_kernel(PrefillParams p) {
         s[rb] = mfma32(as_bf16x8(a), as_bf16x8(qf), ks == 0 ? f32x16{} : s[rb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // Masks from indices, unless every row of the wave sees the whole tile.
     if (!(jt >= lo_max && jt + TN <= hi_min)) {
 #pragma unroll
@@ -319,6 +323,7 @@ void prefill_kernel(PrefillParams p) {
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) lsum[rb] += ps[rb];
+    __builtin_amdgcn_s_setprio(3);
     // O^T += V^T P^T in two 16-key steps; each V^T fragment serves every row block.
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -335,6 +340,7 @@ void prefill_kernel(PrefillParams p) {
         for (int dt = 0; dt < 2; ++dt) o[rb][dt] = mfma32(as_bf16x8(av[dt]), as_bf16x8(pk[rb][kk]), o[rb][dt]);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   // No key is visible (nt = 0): Q is not needed, but its DMA must land before the slice is
   // reused for the output. Every wave is done with the ring before the next pass reuses it.
   WAIT_VMCNT(0);
