@@ -27,13 +27,6 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 // Two fp32 -> packed bf16x2 (RNE) with the gfx950 conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -76,29 +69,16 @@ __device__ __forceinline__ u32x4 join_tr16(s16x4 lo, s16x4 hi) {
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
-// 16-byte load of data read once (KV cache streaming): non-temporal, so it does not displace
-// reusable lines from the caches.
-__device__ __forceinline__ u32x4 load_stream(const uint16_t* ptr) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
-}
-
 // Raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes return zero
 // without touching memory (CDNA buffer range check), so tails need no branches. The range
 // check covers the VGPR offset; the SGPR offset is kept at zero so every byte is checked.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
 
 // 16 bytes per lane from a buffer straight into LDS (no VGPRs): lane i of the wave writes
-// lds_base + 16 * i, where lds_base is wave-uniform.
-__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
-}
-
-// The same 16-byte buffer -> LDS load, issued so that the compiler does not see the LDS write.
+// lds_base + 16 * i, where lds_base is wave-uniform. The load is issued so that the compiler
+// does not see the LDS write.
 // The compiler otherwise makes every later LDS read wait for all outstanding buffer loads
 // (it cannot tell the stages of a ring apart), which serialises a prefetch ring. Callers own
 // the synchronisation: s_waitcnt vmcnt for their own loads, then lds_barrier().
@@ -172,8 +152,6 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
 // s_waitcnt lgkmcnt(0) alone (the vmcnt field at its maximum, 63).
 #define WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14))
-
-__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
