@@ -232,8 +232,11 @@ def summarize(stats_dir, out_md, title, command, workload=None):
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
             rec = json.load(fh).get(workload)
         if rec is not None and rec["source_hash"] == source_hash(kernel_kind(workload)):
+            # paged decode's line also times the planner's chunk length (context), so its counters
+            # are taken with the workload's 512-token chunks alone
+            chunk = " --kv-chunk 512" if workload == "paged_decode" else ""
             lines += ["", f"HBM traffic of `{rec['kernel']}` per launch (rocprofv3 `--pmc FETCH_SIZE`, then `--pmc "
-                          f"WRITE_SIZE`, each in its own run of `bench.py --workload {workload} --steps 2 --warmup 1 "
+                          f"WRITE_SIZE`, each in its own run of `bench.py --workload {workload}{chunk} --steps 2 --warmup 1 "
                           f"--no-cold --no-cpu-baseline`; KiB per dispatch scaled so that a plain 1 GiB copy "
                           f"(`bench.py --calibrate-copy`) reads and writes 1 GiB: fetch x{rec['fetch_scale']}, write "
                           f"x{rec['write_scale']}; recorded by `bench.py --record-traffic`, source hash "
