@@ -23,6 +23,9 @@ constexpr int32_t kMaxColumns = 64;   // q_len * (num_q_heads / num_kv_heads) pe
 // Fixed cost of one split-KV work item (plan, combine, partial, its share of the merge), in
 // keys: fitted to whole-call times of the verify-shaped workloads over chunk lengths 1024-4096.
 constexpr int64_t kPlanItemKeys = 1024;
+// Cost of one merge round trip (8 partials of a row), in keys: the merge lasts as long as its
+// row with the most partials. Fitted to whole-call times over batch 1-64, lengths 2048-32768.
+constexpr int64_t kPlanMergeKeys = 384;
 constexpr int64_t kMaxGridY = 65535;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -326,8 +329,12 @@ attn_sink_status attn_sink_decode_plan_chunk(const int32_t* kv_lens, int32_t bat
   int64_t best = top, best_load = INT64_MAX;
   std::vector<int64_t> load((size_t)grid);
   for (int64_t c = step; c <= top; c += step) {
-    int64_t items = 0;
-    for (int32_t b = 0; b < batch; ++b) items += std::max<int64_t>(1, (std::max(0, kv_lens[b]) + c - 1) / c);
+    int64_t items = 0, most = 1;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t n = std::max<int64_t>(1, (std::max(0, kv_lens[b]) + c - 1) / c);
+      items += n;
+      most = std::max(most, n);
+    }
     items *= num_kv_heads;
     if (items > 64 * grid && c != top) continue;  // much finer than the grid: never the cheapest
     std::fill(load.begin(), load.end(), 0);
@@ -340,7 +347,7 @@ attn_sink_status attn_sink_decode_plan_chunk(const int32_t* kv_lens, int32_t bat
         for (int32_t h = 0; h < num_kv_heads; ++h, ++i) load[(size_t)(i % grid)] += keys + kPlanItemKeys;
       }
     }
-    const int64_t worst = *std::max_element(load.begin(), load.end());
+    const int64_t worst = *std::max_element(load.begin(), load.end()) + kPlanMergeKeys * ((most + 7) / 8);
     if (worst <= best_load) {  // ties go to the longer chunk (fewer partials to merge)
       best_load = worst;
       best = c;

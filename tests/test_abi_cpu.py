@@ -408,10 +408,11 @@ def _plan(amd, lens, q_len=5, hq=64, hkv=8, page=16, wgs=512):
     return st, out.value
 
 
-def _plan_model(lens, hkv, page, wgs, item_keys=1024):
+def _plan_model(lens, hkv, page, wgs, item_keys=1024, merge_keys=384):
     """The planner's documented rule, written out: deal (sequence, chunk, KV head) items
-    round-robin to wgs workgroups, charge keys + item_keys each, keep the chunk whose most loaded
-    workgroup is lightest (ties: the longer chunk)."""
+    round-robin to wgs workgroups, charge keys + item_keys each, add merge_keys per 8 partials
+    of the sequence with the most chunks, keep the chunk with the lowest cost (ties: the longer
+    chunk)."""
     step = max(256, page)
     top = max(step, -(-max([0] + list(lens)) // step) * step)
     best = None
@@ -428,7 +429,8 @@ def _plan_model(lens, hkv, page, wgs, item_keys=1024):
                 for _ in range(hkv):
                     load[i % wgs] += keys + item_keys
                     i += 1
-        w = max(load)
+        most = max([1] + [max(1, -(-max(0, L) // c)) for L in lens])
+        w = max(load) + merge_keys * -(-most // 8)
         if best is None or w <= best[0]:
             best = (w, c)
     return best[1]
