@@ -548,13 +548,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   if (nt > 0) {
     // Wave w loads rows [8w, 8w + 8) of a tile's K and V (one 1 KB load each); lane i writes
-    // chunk position i & 7 of row i >> 3, with the same swizzles as the 4-wave kernel.
-    // The per-lane part of the offsets is rebuilt from the lane id at every issue: kept in
-    // registers across the pass, it would be spilled, and each reload would wait for every
-    // tile in flight.
-    // Per-lane parts of a tile's load offsets (contiguous layout), kept for the pass: lane i
-    // writes chunk position i & 7 of row 8 w + (i >> 3), which holds global chunk (i & 7) ^ f(row);
-    // (r >> 1) & 7 and ((r >> 1) & 1) * 4 for r = 8 w + r8.
+    // chunk position i & 7 of row 8 w + (i >> 3), which holds global chunk (i & 7) ^ f(row), with
+    // f(r) = (r >> 1) & 7 for K and ((r >> 1) & 1) * 4 for V, the swizzles of the 4-wave kernel.
+    // Contiguous layout: the per-lane parts of the offsets are computed once and kept for the
+    // pass. Paged layout: they are rebuilt from the lane id at every issue, beside the page's
+    // buffer descriptor; kept in registers across the pass they would be spilled, and each
+    // reload would wait for every tile in flight.
     uint32_t k_lane = 0, v_lane = 0;
     if constexpr (!PAGED) {
       const int ln = opaque_lane_id();
