@@ -113,11 +113,39 @@ def f64(bits):
     return bf16_bits_to_f32(bits).astype(np.float64)
 
 
+def code_only(text):
+    """C++ source text without its comments, whitespace runs collapsed to one space: what the
+    compiler sees, so that editing a comment does not orphan a counter record."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":  # string or character literal, copied whole
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(kind):
+    """Hash of the code (comments and layout aside) of the sources a kernel kind is built from."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "gqa_attention_sinks_sink_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "gqa_attention_sinks_sink_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode("utf-8"))
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 
