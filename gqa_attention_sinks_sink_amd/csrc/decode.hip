@@ -178,7 +178,9 @@ void decode_split_kernel(DecodeParams p) {
     Loc r;
     const int P = item / p.hkv;
     r.kvh = item - P * p.hkv;
-    while (P >= cur_before + win_total) {
+    // (P < the pair count, so a later window holds it; the batch bound keeps the walk finite even
+    // if kv_lens changed since the count was taken.)
+    while (P >= cur_before + win_total && cur_base + 64 < p.batch) {
       cur_before += win_total;
       cur_base += 64;
       load_window();
