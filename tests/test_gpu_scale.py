@@ -149,3 +149,30 @@ def test_prefill_more_than_256_query_heads(amd):
                                    inp["cu_seqlens"], inp["sinks"], spec.scale, True, 0)
     assert_close(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
                  "prefill hq 320")
+
+
+@pytest.mark.parametrize("seqlen,hq,hkv,causal,window", [(32768, 8, 1, True, 0), (16384, 16, 2, False, 0),
+                                                         (6000, 16, 2, True, 1500)])
+def test_prefill_long_sequences_sampled(amd, seqlen, hq, hkv, causal, window):
+    """Sequences far longer than the workloads' 4096 tokens: the causal 8-wave kernel over 512
+    row blocks, the bidirectional one over 16K keys per row, and the 4-wave kernel with a 1500-key
+    window (about 48 tiles per pass, masked at both ends). Sampled rows of the long sequence (block
+    edges, the middle, the tail) and every row of a short second sequence."""
+    spec = scaled(CONFIGS["causal_prefill"], batch=2, hq=hq, hkv=hkv, causal=causal, window=window,
+                  seed=980 + hq + window)
+    inp = make_varlen(spec, seqlens=[seqlen, 777])
+    rng = np.random.default_rng(980 + seqlen)
+    picks = {0, 1, 63, 64, 511, 512, 4095, 4096, seqlen // 2, seqlen - 65, seqlen - 64, seqlen - 1}
+    picks |= set(rng.integers(0, seqlen, size=8).tolist())
+    rows = {0: sorted(picks), 1: list(range(777))}
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(DEV)
+    print(f"prefill seqlen {seqlen} hq {hq} hkv {hkv} causal {causal} window {window}", flush=True)
+    out, lse = amd.attn_sink_prefill(tbits(inp["q"]), tbits(inp["k"]), tbits(inp["v"]),
+                                     torch.from_numpy(inp["sinks"]).to(DEV), cu, cu, seqlen, seqlen, spec.scale,
+                                     causal, window)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_varlen(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), inp["cu_seqlens"],
+                                   inp["cu_seqlens"], inp["sinks"], spec.scale, causal, window, seqs=[0, 1],
+                                   rows=rows)
+    assert_close(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
+                 f"prefill seqlen {seqlen} causal {causal} window {window}")
