@@ -176,3 +176,24 @@ def test_prefill_long_sequences_sampled(amd, seqlen, hq, hkv, causal, window):
                                    rows=rows)
     assert_close(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
                  f"prefill seqlen {seqlen} causal {causal} window {window}")
+
+
+@pytest.mark.parametrize("q_len,chunk", [(1, 0), (1, 16384), (4, 3072), (1, -1)])
+def test_decode_one_very_long_sequence(amd, q_len, chunk):
+    """65536 keys in one sequence next to a short one: with one chunk per sequence (chunk 0) an item
+    holds 4096 page groups, so every wave walks its page ids through 16 segments of 64 groups.
+    chunk -1 takes the planner's choice for this batch."""
+    spec = scaled(CONFIGS["verify"], batch=2, q_len=q_len, kv_len=(q_len, 65536), hq=16, hkv=2, kv_chunk=max(chunk, 0),
+                  seed=990 + q_len)
+    inp = make_paged(spec, kv_lens=[65536, 1000 + q_len])
+    if chunk < 0:
+        chunk = amd.attn_sink_decode_plan_chunk(inp["kv_lens"], q_len, spec.hq, spec.hkv, spec.page_size)
+    d = device_paged(inp)
+    print(f"decode 65536 keys q_len {q_len} chunk {chunk}", flush=True)
+    out, lse = amd.attn_sink_decode_paged(d["q"], d["k"], d["v"], d["table"], d["lens"], d["sinks"], q_len,
+                                          inp["max_kv_len"], spec.scale, True, 0, chunk)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"]), inp["page_table"],
+                                 inp["kv_lens"], inp["sinks"], q_len, spec.scale, True, 0)
+    assert_close(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
+                 f"decode 65536 keys q_len {q_len} chunk {chunk}")
