@@ -197,3 +197,31 @@ def test_decode_one_very_long_sequence(amd, q_len, chunk):
                                  inp["kv_lens"], inp["sinks"], q_len, spec.scale, True, 0)
     assert_close(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
                  f"decode 65536 keys q_len {q_len} chunk {chunk}")
+
+
+@pytest.mark.parametrize("lq,lk,causal,window", [((300, 50, 9), (100, 0, 9), True, 0), ((300, 50, 9), (100, 0, 9), True, 40),
+                                                 ((300, 50, 9), (100, 0, 9), False, 0),
+                                                 ((2100, 64), (500, 64), True, 0), ((2100, 64), (500, 2100), False, 0)])
+def test_prefill_more_queries_than_keys(amd, lq, lk, causal, window):
+    """Queries are the last tokens of their sequence, so with more query tokens than keys the first
+    Lq - Lk rows have no causal key (out 0, LSE the sink), and a sequence with no keys at all gives
+    every row that. The 4-wave kernel (the first three cases) and the 8-wave one (2100 query
+    tokens, no window)."""
+    spec = scaled(CONFIGS["causal_prefill"], batch=len(lq), hq=16, hkv=2, causal=causal, window=window,
+                  seed=1000 + lq[0] + window)
+    inp = make_varlen(spec, seqlens=list(lq))
+    rng = np.random.default_rng(1000 + lk[0])
+    lk = np.asarray(lk)
+    cu_kv = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    from workloads import bf16_round_bits
+    k = bf16_round_bits(rng.standard_normal((int(lk.sum()), 2, 64), dtype=np.float32))
+    v = bf16_round_bits(rng.standard_normal((int(lk.sum()), 2, 64), dtype=np.float32))
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(DEV)
+    print(f"prefill lq {lq} lk {tuple(lk)} causal {causal} window {window}", flush=True)
+    out, lse = amd.attn_sink_prefill(tbits(inp["q"]), tbits(k), tbits(v), torch.from_numpy(inp["sinks"]).to(DEV), cu,
+                                     torch.from_numpy(cu_kv).to(DEV), max(lq), int(lk.max()), spec.scale, causal, window)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_varlen(f64(inp["q"]), f64(k), f64(v), inp["cu_seqlens"], cu_kv, inp["sinks"], spec.scale,
+                                   causal, window)
+    assert_close(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
+                 f"prefill lq {lq} lk {tuple(lk)} causal {causal} window {window}")
