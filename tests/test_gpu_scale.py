@@ -225,3 +225,27 @@ def test_prefill_more_queries_than_keys(amd, lq, lk, causal, window):
                                    causal, window)
     assert_close(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
                  f"prefill lq {lq} lk {tuple(lk)} causal {causal} window {window}")
+
+
+def test_merge_rows_of_many_partials(amd):
+    """Rows of 0 to 150 partials (the merge folds 8 at a time), LSEs spread over +-80 with empty
+    (-inf) partials mixed in, against the oracle's merge row by row."""
+    rng = np.random.default_rng(1010)
+    counts = np.array([0, 1, 7, 8, 9, 16, 17, 63, 64, 65, 150] + rng.integers(0, 40, size=21).tolist())
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    n, hq = int(indptr[-1]), 4
+    o_p = rng.standard_normal((n, hq, 64)).astype(np.float32)
+    l_p = (rng.uniform(-80, 80, size=(n, hq))).astype(np.float32)
+    l_p[rng.random((n, hq)) < 0.2] = -np.inf
+    print(f"merge of {len(counts)} rows, {n} partials", flush=True)
+    out, lse = amd.attn_sink_merge_partials(torch.from_numpy(o_p).to(DEV), torch.from_numpy(l_p).to(DEV),
+                                            torch.from_numpy(indptr).to(DEV))
+    torch.cuda.synchronize()
+    ro = np.zeros((len(counts), hq, 64))
+    rl = np.full((len(counts), hq), -np.inf)
+    for r in range(len(counts)):
+        a, b = int(indptr[r]), int(indptr[r + 1])
+        if b > a:
+            ro[r], rl[r] = oracle.merge(o_p[a:b].astype(np.float64), l_p[a:b].astype(np.float64))
+    assert_close(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
+                 "merge of many partials")
