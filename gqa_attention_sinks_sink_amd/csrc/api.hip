@@ -34,6 +34,12 @@ inline bool misaligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(
 
 inline bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// A sequence's capacity in tokens (its page-table row times the page size) is an int32 in the
+// kernels, which bound every sequence length by it.
+inline bool capacity_fits(int32_t max_pages_per_seq, int32_t page_size) {
+  return (int64_t)max_pages_per_seq * page_size <= INT32_MAX;
+}
+
 inline int32_t ilog2(int32_t x) {
   int32_t s = 0;
   while ((1 << s) < x) ++s;
@@ -187,6 +193,7 @@ attn_sink_status attn_sink_prefill_paged(const void* q, const void* k_cache, con
   if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_SINK_ERR_INVALID_ARG;
   if (head_dim != kSupportedHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
   if (!is_pow2(page_size) || page_size < 16 || page_size > 256) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (!capacity_fits(max_pages_per_seq, page_size)) return ATTN_SINK_ERR_UNSUPPORTED;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || page_table == nullptr || kv_lens == nullptr ||
       cu_seqlens_q == nullptr || out == nullptr)
@@ -247,6 +254,7 @@ attn_sink_status attn_sink_rope_append(const void* q, const void* k, const void*
   if (yarn_factor > 1.f && yarn_ramp == ATTN_SINK_YARN_RAMP_INDEX && !(yarn_alpha > 0.f)) return ATTN_SINK_ERR_INVALID_ARG;
   if (head_dim != kSupportedHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
   if (!is_pow2(page_size) || page_size < 16 || page_size > 256) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (!capacity_fits(max_pages_per_seq, page_size)) return ATTN_SINK_ERR_UNSUPPORTED;
   if (batch > kMaxGridY) return ATTN_SINK_ERR_UNSUPPORTED;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
   if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr || kv_lens == nullptr ||
@@ -405,6 +413,7 @@ attn_sink_status decode_prepare(const void* q, const void* k_cache, const void* 
   const int32_t group = num_q_heads / num_kv_heads;
   if ((int64_t)q_len * group > kMaxColumns) return ATTN_SINK_ERR_UNSUPPORTED;
   if (!is_pow2(page_size) || page_size < 16 || page_size > 256) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (!capacity_fits(max_pages_per_seq, page_size)) return ATTN_SINK_ERR_UNSUPPORTED;
   if (kv_chunk > 0 && (kv_chunk % 64 != 0 || kv_chunk % page_size != 0)) return ATTN_SINK_ERR_UNSUPPORTED;
   if (num_kv_heads > kMaxGridY) return ATTN_SINK_ERR_UNSUPPORTED;
   const int64_t chunk = effective_chunk(kv_chunk, max_kv_len, page_size);

@@ -39,6 +39,8 @@
  *     ATTN_SINK_ERR_UNSUPPORTED, with nothing launched. A failed launch returns
  *     ATTN_SINK_ERR_HIP. Device-side faults surface at the caller's next
  *     synchronisation. Nothing aborts the process.
+ *   - Paged entry points: a sequence's capacity, max_pages_per_seq * page_size tokens,
+ *     must be below 2^31, else ATTN_SINK_ERR_UNSUPPORTED.
  *   - Memory safety against bad device metadata: sequence lengths, cu_seqlens offsets and
  *     page ids read on the device are clamped into the ranges the host scalars declare,
  *     so inconsistent metadata yields wrong numbers for the affected rows, never an

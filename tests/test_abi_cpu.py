@@ -134,6 +134,8 @@ def test_prefill_paged_argument_errors(amd):
     assert _prefill_paged(amd, scale=float("nan")) == INVALID
     assert _prefill_paged(amd, batch=-1) == INVALID
     assert _prefill_paged(amd, max_pages=0) == INVALID
+    assert _prefill_paged(amd, max_pages=1 << 23, page=256) == UNSUPPORTED   # capacity 2^31 tokens
+    assert _prefill_paged(amd, max_pages=(1 << 23) - 1, page=256, batch=0) == OK
     assert _prefill_paged(amd, num_pages=0) == INVALID
     for name in ("q", "kc", "vc", "table", "cu_q", "lens", "out"):
         assert _prefill_paged(amd, **{name: None}) == INVALID, name
@@ -224,6 +226,7 @@ def test_rope_append_argument_errors(amd):
     assert _rope(amd, ramp=1, batch=0) == OK
     assert _rope(amd, hq=6, hkv=4) == INVALID
     assert _rope(amd, max_pages=0) == INVALID
+    assert _rope(amd, max_pages=1 << 27, page=16) == UNSUPPORTED              # capacity 2^31 tokens
     for name in ("q", "k", "v", "cu_q", "lens", "table", "kc", "vc", "q_out"):
         assert _rope(amd, **{name: None}) == INVALID, name
     # no YaRN scaling: original length and ramp bounds are not needed
@@ -245,6 +248,8 @@ def test_decode_argument_errors(amd):
     assert _decode(amd, scale=-1.0) == INVALID
     assert _decode(amd, num_pages=0) == INVALID
     assert _decode(amd, max_pages=0) == INVALID
+    assert _decode(amd, max_pages=1 << 27, page=16) == UNSUPPORTED            # capacity 2^31 tokens
+    assert _decode_tree(amd, max_pages=1 << 24, page=128) == UNSUPPORTED
     assert _decode(amd, max_kv=-1) == INVALID
     assert _decode(amd, q=None) == INVALID
     assert _decode(amd, table=None) == INVALID
