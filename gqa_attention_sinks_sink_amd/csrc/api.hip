@@ -23,7 +23,7 @@ constexpr int32_t kMaxColumns = 64;   // q_len * (num_q_heads / num_kv_heads) pe
 // Fixed cost of one split-KV work item (plan, combine, partial, its share of the merge), in
 // keys: fitted to whole-call times of the verify-shaped workloads over chunk lengths 1024-4096.
 constexpr int64_t kPlanItemKeys = 1024;
-// Cost of one merge round trip (8 partials of a row), in keys: the merge lasts as long as its
+// Cost of one merge round trip (16 partials of a row), in keys: the merge lasts as long as its
 // row with the most partials. Fitted to whole-call times over batch 1-64, lengths 2048-32768.
 constexpr int64_t kPlanMergeKeys = 384;
 constexpr int64_t kMaxGridY = 65535;
@@ -355,7 +355,7 @@ attn_sink_status attn_sink_decode_plan_chunk(const int32_t* kv_lens, int32_t bat
         for (int32_t h = 0; h < num_kv_heads; ++h, ++i) load[(size_t)(i % grid)] += keys + kPlanItemKeys;
       }
     }
-    const int64_t worst = *std::max_element(load.begin(), load.end()) + kPlanMergeKeys * ((most + 7) / 8);
+    const int64_t worst = *std::max_element(load.begin(), load.end()) + kPlanMergeKeys * ((most + 15) / 16);
     if (worst <= best_load) {  // ties go to the longer chunk (fewer partials to merge)
       best_load = worst;
       best = c;

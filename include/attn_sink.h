@@ -363,9 +363,9 @@ attn_sink_status attn_sink_decode_paged_tree_partials(
  * multiples of max(256, page_size) up to one chunk per sequence) this function deals the
  * items the same way. It charges each item its keys plus a fixed cost of 1024 keys, which
  * was fitted on MI355X to whole-call times of the verify-shaped workloads. The merge reads a
- * sequence's partials 8 at a time, so it adds 384 keys per 8 chunks (rounded up) of the
- * sequence with the most chunks; that cost was fitted to whole-call times over batches of
- * 1-64 sequences of 2048-32768 keys. The cost of a candidate is its most loaded workgroup's
+ * sequence's partials 16 per memory round trip, so it adds 384 keys per 16 chunks (rounded
+ * up) of the sequence with the most chunks; that cost was fitted to whole-call times over
+ * batches of 1-64 sequences of 2048-32768 keys. The cost of a candidate is its most loaded workgroup's
  * load plus that merge cost. It returns the candidate of lowest cost; ties go to the longer
  * chunk.
  *   kv_lens      int32 [batch] on the HOST: the lengths the call will see.

@@ -415,7 +415,7 @@ def _plan(amd, lens, q_len=5, hq=64, hkv=8, page=16, wgs=512):
 
 def _plan_model(lens, hkv, page, wgs, item_keys=1024, merge_keys=384):
     """The planner's documented rule, written out: deal (sequence, chunk, KV head) items
-    round-robin to wgs workgroups, charge keys + item_keys each, add merge_keys per 8 partials
+    round-robin to wgs workgroups, charge keys + item_keys each, add merge_keys per 16 partials
     of the sequence with the most chunks, keep the chunk with the lowest cost (ties: the longer
     chunk)."""
     step = max(256, page)
@@ -435,7 +435,7 @@ def _plan_model(lens, hkv, page, wgs, item_keys=1024, merge_keys=384):
                     load[i % wgs] += keys + item_keys
                     i += 1
         most = max([1] + [max(1, -(-max(0, L) // c)) for L in lens])
-        w = max(load) + merge_keys * -(-most // 8)
+        w = max(load) + merge_keys * -(-most // 16)
         if best is None or w <= best[0]:
             best = (w, c)
     return best[1]

@@ -228,8 +228,8 @@ def test_prefill_more_queries_than_keys(amd, lq, lk, causal, window):
 
 
 def test_merge_rows_of_many_partials(amd):
-    """Rows of 0 to 150 partials (the merge folds 8 at a time), LSEs spread over +-80 with empty
-    (-inf) partials mixed in, against the oracle's merge row by row."""
+    """Rows of 0 to 150 partials (the merge reads 16 per round trip, in two groups of 8), LSEs
+    spread over +-80 with empty (-inf) partials mixed in, against the oracle's merge row by row."""
     rng = np.random.default_rng(1010)
     counts = np.array([0, 1, 7, 8, 9, 16, 17, 63, 64, 65, 150] + rng.integers(0, 40, size=21).tolist())
     indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
